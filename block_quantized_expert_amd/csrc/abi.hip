@@ -1,0 +1,238 @@
+// abi.hip -- host side of the C ABI: argument validation, the image and
+// workspace layouts, the launch plan of a decode step, status strings.
+//
+// Layer definition: page "Lucebox专攻DeepSeek V4…" (m.mzlw.cn), section
+// "MoE 专家并行" (256 routed experts, top-6, 1 shared); page "APU 实现 token
+// 自由…" (ainomam.com), section "Lucebox 的优化三板斧" (TOP-K/ARGSORT routing,
+// decode-once for all verify columns).  Everything here runs on the host
+// before any launch; nothing here touches device memory.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "rfpx_impl.hpp"
+
+namespace rfpx {
+
+static thread_local char g_err[512];
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+rfpx_status fail(rfpx_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+size_t image_layout(int d, int f, int E, const int *fmts, ExpertDesc *desc) {
+  size_t off = align_up(kImgTable + (size_t)(E + 1) * sizeof(ExpertDesc), 256);
+  for (int e = 0; e <= E; ++e) {
+    for (int m = 0; m < 3; ++m) {
+      int fmt = fmts[3 * e + m];
+      size_t rows = m < 2 ? f : d, cols = m < 2 ? d : f;
+      size_t nblk = rows * (cols / 32);
+      if (desc) {
+        desc[e].codes[m] = off;
+        desc[e].fmt[m] = fmt;
+      }
+      off = align_up(off + nblk * code_bytes(fmt), 256);
+      if (desc) desc[e].scales[m] = off;
+      off = align_up(off + nblk * scale_bytes(fmt), 256);
+    }
+    if (desc) desc[e].reserved = 0;
+  }
+  return off;
+}
+
+namespace {
+
+bool pow2_in(int v, int lo, int hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+// Rows per workgroup tile for a set of formats: every format must fit in
+// 1..wmax waves of r rows (rpi rows per wave step), the tile must divide
+// `rows`, and (gate/up) hold whole 32-row blocks of h.
+bool pick_tile(const Geo *geo, unsigned fmts, int r, int wmax, int rows,
+               bool need32, int *rw) {
+  int lo = need32 ? 32 : 1, hi = rows;
+  for (int f = RFPX_FP2; f <= RFPX_FP4; ++f) {
+    if (!((fmts >> f) & 1u)) continue;
+    lo = lo > geo[f].rpi * r ? lo : geo[f].rpi * r;
+    hi = hi < geo[f].rpi * r * wmax ? hi : geo[f].rpi * r * wmax;
+  }
+  if (hi < lo || rows % hi) return false;
+  *rw = hi;
+  return true;
+}
+
+rfpx_status check_layer(const moe_layer *L) {
+  if (!L) return fail(RFPX_E_ARG, "layer is null");
+  if (!L->fmts) return fail(RFPX_E_ARG, "layer format table is null");
+  if (!pow2_in(L->d, 256, 4096))
+    return fail(RFPX_E_SHAPE, "d=%d: must be a power of two in [256, 4096]", L->d);
+  if (!pow2_in(L->f, 64, 4096))
+    return fail(RFPX_E_SHAPE, "f=%d: must be a power of two in [64, 4096]", L->f);
+  if (L->n_experts < 1 || L->n_experts > kEMax)
+    return fail(RFPX_E_SHAPE, "n_experts=%d: must be in [1, %d]", L->n_experts, kEMax);
+  if (L->top_k < 1 || L->top_k > kKMax || L->top_k > L->n_experts)
+    return fail(RFPX_E_SHAPE, "top_k=%d: must be in [1, min(E, %d)]", L->top_k, kKMax);
+  for (int i = 0; i < 3 * (L->n_experts + 1); ++i)
+    if (!valid_fmt(L->fmts[i]))
+      return fail(RFPX_E_FORMAT, "format table entry %d is %d", i, L->fmts[i]);
+  for (int e = 0; e <= L->n_experts; ++e)
+    if (L->fmts[3 * e] != L->fmts[3 * e + 1])
+      return fail(RFPX_E_FORMAT, "expert %d: gate and up formats differ", e);
+  return RFPX_OK;
+}
+
+// Everything a decode step needs that depends only on shapes and formats.
+rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
+  rfpx_status st = check_layer(L);
+  if (st) return st;
+  if (q < 1 || q > kQMax) return fail(RFPX_E_SHAPE, "q=%d: must be in [1, %d]", q, kQMax);
+  if (xtype != RFPX_X_F32 && xtype != RFPX_X_BF16)
+    return fail(RFPX_E_ARG, "xtype=%d", xtype);
+  memset(p, 0, sizeof *p);
+  p->d = L->d;
+  p->f = L->f;
+  p->E = L->n_experts;
+  p->k = L->top_k;
+  p->q = q;
+  p->xtype = xtype;
+  p->routed_scale = L->routed_scale;
+  p->router_w = L->router_w;
+  p->image = L->image;
+  for (int e = 0; e <= L->n_experts; ++e) {
+    p->prep_fmts |= 1u << L->fmts[3 * e];
+    p->down_fmts |= 1u << L->fmts[3 * e + 2];
+  }
+  for (int f = RFPX_FP2; f <= RFPX_FP4; ++f) {
+    if ((p->prep_fmts >> f) & 1u) {
+      if (!make_geo(f, L->d, &p->geo_gu[f]) || p->geo_gu[f].tpl > 2)
+        return fail(RFPX_E_SHAPE, "d=%d does not tile for gate/up format %d", L->d, f);
+    }
+    if ((p->down_fmts >> f) & 1u) {
+      if (!make_geo(f, L->f, &p->geo_dn[f]) || p->geo_dn[f].tpl > 2)
+        return fail(RFPX_E_SHAPE, "f=%d does not tile for down format %d", L->f, f);
+    }
+  }
+  p->g = q == 1 ? 1 : 2;
+  p->r = 4;     // rows per wave: must match the kernels' R template
+  p->wmax = 8;  // waves per workgroup
+  if (!pick_tile(p->geo_gu, p->prep_fmts, p->r, p->wmax, L->f, true, &p->rw_gu))
+    return fail(RFPX_E_SHAPE, "f=%d: no gate/up tile for this format mix", L->f);
+  if (!pick_tile(p->geo_dn, p->down_fmts, p->r, p->wmax, L->d, false, &p->rw_dn))
+    return fail(RFPX_E_SHAPE, "d=%d: no down tile for this format mix", L->d);
+
+  WsLayout &w = p->wl;
+  const int vx = xtype == RFPX_X_BF16 ? 1 : 2;
+  const int nb_d = L->d / 32, nb_f = L->f / 32;
+  w.max_slots = 1 + (q * L->top_k < L->n_experts ? q * L->top_k : L->n_experts);
+  w.n_tiles_down = L->d / p->rw_dn;
+  size_t off = 0;
+  w.counters = off;
+  off = align_up(off + (size_t)(1 + w.n_tiles_down) * 4, 256);
+  w.route = off;
+  off = align_up(off + sizeof(RouteTable), 256);
+  w.scores = off;
+  off = align_up(off + (size_t)q * L->n_experts * 4, 256);
+  w.xp = off;
+  off = align_up(off + (size_t)3 * q * nb_d * vx * 16 * 4, 256);
+  w.xnc = off;
+  off = align_up(off + (size_t)3 * q * nb_d * 4, 256);
+  w.hp = off;
+  off = align_up(off + (size_t)w.max_slots * q * nb_f * 32 * 4, 256);
+  w.hnc = off;
+  off = align_up(off + (size_t)w.max_slots * q * nb_f * 4, 256);
+  w.part = off;
+  off = align_up(off + (size_t)w.max_slots * q * L->d * 4, 256);
+  w.total = off;
+  return RFPX_OK;
+}
+
+rfpx_status check_run(const moe_layer *L, const ForwardPlan &p, const void *x,
+                      void *ws, size_t ws_bytes) {
+  if (!L->router_w || !L->image) return fail(RFPX_E_ARG, "layer router or image is null");
+  if (!x) return fail(RFPX_E_ARG, "x is null");
+  if (!ws) return fail(RFPX_E_ARG, "workspace is null");
+  if ((uintptr_t)ws % 256) return fail(RFPX_E_ALIGN, "workspace not 256-byte aligned");
+  if ((uintptr_t)L->image % 256) return fail(RFPX_E_ALIGN, "image not 256-byte aligned");
+  if ((uintptr_t)L->router_w % 16 || (uintptr_t)x % 16)
+    return fail(RFPX_E_ALIGN, "router weights and x must be 16-byte aligned");
+  if (ws_bytes < p.wl.total)
+    return fail(RFPX_E_WORKSPACE, "workspace holds %zu bytes, needs %zu", ws_bytes, p.wl.total);
+  return RFPX_OK;
+}
+
+}  // namespace
+}  // namespace rfpx
+
+using namespace rfpx;
+
+extern "C" {
+
+const char *rfpx_status_str(int st) {
+  switch (st) {
+    case RFPX_OK: return "ok";
+    case RFPX_E_ARG: return "bad argument";
+    case RFPX_E_SHAPE: return "unsupported shape";
+    case RFPX_E_ALIGN: return "misaligned pointer";
+    case RFPX_E_FORMAT: return "bad format table or image";
+    case RFPX_E_WORKSPACE: return "workspace or output too small";
+    case RFPX_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *rfpx_last_error(void) { return g_err; }
+
+size_t moe_workspace_bytes(const moe_layer *L, int q_or_T, int prefill) {
+  ForwardPlan p;
+  if (prefill) return 0;  // the prefill path sizes its own workspace (prefill.hip)
+  if (make_plan(L, q_or_T, RFPX_X_F32, &p)) return 0;  // fp32 x needs the most
+  return p.wl.total;
+}
+
+rfpx_status moe_route_topk(const moe_layer *L, const void *x, int xtype, int q,
+                           int32_t *ids, float *w, void *ws, size_t ws_bytes,
+                           void *stream) {
+  ForwardPlan p;
+  rfpx_status st = make_plan(L, q, xtype, &p);
+  if (st) return st;
+  if ((st = check_run(L, p, x, ws, ws_bytes))) return st;
+  if (!ids || !w) return fail(RFPX_E_ARG, "ids or w is null");
+  p.x = x;
+  p.ids_out = ids;
+  p.w_out = w;
+  p.ws = static_cast<uint8_t *>(ws);
+  p.route_only = true;
+  p.stream = (hipStream_t)stream;
+  hipError_t e = launch_route(p);
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_route_topk: %s", hipGetErrorString(e));
+}
+
+rfpx_status moe_layer_forward(const moe_layer *L, const void *x, int xtype, int q,
+                              float *y, void *ws, size_t ws_bytes, void *stream) {
+  ForwardPlan p;
+  rfpx_status st = make_plan(L, q, xtype, &p);
+  if (st) return st;
+  if ((st = check_run(L, p, x, ws, ws_bytes))) return st;
+  if (!y) return fail(RFPX_E_ARG, "y is null");
+  p.x = x;
+  p.y = y;
+  p.ws = static_cast<uint8_t *>(ws);
+  p.stream = (hipStream_t)stream;
+  hipError_t e = launch_route(p);
+  if (e == hipSuccess) e = launch_experts(p);
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_layer_forward: %s", hipGetErrorString(e));
+}
+
+}  // extern "C"

@@ -1,0 +1,352 @@
+// codec.hip -- ROCmFP2/FP3/FP4 block codec on the GPU and the device image
+// of a layer's experts.
+//
+// Formats: page "DeepSeek V4 Flash 在 128GB 锐龙 AI MAX+ 上跑到 32 tok/s"
+// (taozi.news), section "ROCmFPX：把 284B 权重压进 128 GB": 32 weights per
+// block, FP2 10 bytes (2.50 bit/weight), FP3 ~3.50, FP4 ~4.25.  Bit layout,
+// quantizer rule and image layout are the ones fixed in include/rfpx.h.
+//
+// All kernels here run once per model load (packing, image build) or in
+// checks (unpack); one thread handles one 32-weight block.
+#include <math.h>
+
+#include "rfpx_impl.hpp"
+
+namespace rfpx {
+namespace {
+
+constexpr int kThreads = 256;
+
+// Code j of a block (FP2/FP3/FP4) from its little-endian code bytes.
+__device__ inline int get_code(int fmt, const uint8_t *b, int j) {
+  int nbit = fmt;  // 2, 3, 4 bits per code
+  int pos = nbit * j;
+  uint32_t two = (uint32_t)b[pos >> 3] | ((uint32_t)b[(pos >> 3) + 1] << 8);
+  return (int)((two >> (pos & 7)) & ((1u << nbit) - 1u));
+}
+
+__device__ inline float code_offset_f(int fmt) {
+  return fmt == RFPX_FP2 ? 1.5f : fmt == RFPX_FP3 ? 3.5f : 7.5f;
+}
+
+// double -> IEEE half bits, round to nearest even, by integer manipulation
+// of the binary64 encoding.
+__device__ inline uint16_t dbl_to_half_rne(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  uint16_t sign = (uint16_t)((u >> 48) & 0x8000u);
+  u &= 0x7FFFFFFFFFFFFFFFull;
+  int ex = (int)(u >> 52);
+  uint64_t frac = u & 0xFFFFFFFFFFFFFull;
+  if (ex == 0x7FF) return (uint16_t)(sign | (frac ? 0x7E00u : 0x7C00u));
+  if (ex == 0) return sign;  // zero, or a double subnormal far below 2^-25
+  int E = ex - 1023;
+  if (E > 15) return (uint16_t)(sign | 0x7C00u);
+  uint64_t m = frac | (1ull << 52);  // value = m * 2^(E-52)
+  int shift = E >= -14 ? 42 : 42 + (-14 - E);
+  if (shift > 63) return sign;
+  uint64_t q = m >> shift;
+  uint64_t rem = m & ((1ull << shift) - 1ull);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1ull))) ++q;
+  if (E >= -14) {
+    if (q == 2048) {
+      q = 1024;
+      if (++E > 15) return (uint16_t)(sign | 0x7C00u);
+    }
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(q - 1024));
+  }
+  return (uint16_t)(sign | (uint16_t)q);  // 1024 is the smallest normal
+}
+
+// ceil(log2(v)) for a positive normal double, from its exponent and fraction.
+__device__ inline int ceil_log2_pos(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  int e = (int)((u >> 52) & 0x7FF) - 1023;
+  return (u & 0xFFFFFFFFFFFFFull) ? e + 1 : e;
+}
+
+template <int FMT>
+__device__ inline void write_block(uint8_t *dst, const int *codes,
+                                   uint32_t scale_bits) {
+  constexpr int NB = FMT;
+  constexpr int CB = code_bytes(FMT);
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    int pos = NB * j;
+    uint64_t v = (uint64_t)(uint32_t)codes[j] << (pos & 31);
+    words[pos >> 5] |= (uint32_t)v;
+    if ((pos & 31) + NB > 32) words[(pos >> 5) + 1] |= (uint32_t)(v >> 32);
+  }
+#pragma unroll
+  for (int i = 0; i < CB; ++i) dst[i] = (uint8_t)(words[i >> 2] >> (8 * (i & 3)));
+  if (FMT == RFPX_FP4) {
+    dst[16] = (uint8_t)scale_bits;
+  } else {
+    dst[CB] = (uint8_t)(scale_bits & 0xFF);
+    dst[CB + 1] = (uint8_t)(scale_bits >> 8);
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_pack(const float *__restrict__ w,
+                                                   long long nblk,
+                                                   uint8_t *__restrict__ out) {
+  long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= nblk) return;
+  constexpr int BB = blk_bytes(FMT);
+  constexpr double O = FMT == RFPX_FP2 ? 1.5 : FMT == RFPX_FP3 ? 3.5 : 7.5;
+  constexpr double CMAX = (double)((1 << FMT) - 1);
+  const float *src = w + i * 32;
+  float v[32];
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    v[j] = src[j];
+    a = fmaxf(a, fabsf(v[j]));
+  }
+  uint8_t *dst = out + i * BB;
+  int c[32];
+  if (a == 0.f) {
+#pragma unroll
+    for (int j = 0; j < BB; ++j) dst[j] = 0;
+    return;
+  }
+  if (FMT == RFPX_FP4) {
+    int e = 127 + ceil_log2_pos((double)a / O);
+    e = e < 1 ? 1 : (e > 254 ? 254 : e);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      double t = rint(ldexp((double)v[j], 127 - e) + O);
+      c[j] = (int)fmin(fmax(t, 0.0), CMAX);
+    }
+    write_block<FMT>(dst, c, (uint32_t)e);
+    return;
+  }
+  uint16_t s16 = dbl_to_half_rne((double)a / O);
+  if ((s16 & 0x7FFFu) == 0x7C00u) s16 = 0x7BFF;  // clamp to 65504
+  double s = (double)half_bits_to_float(s16);
+  if (s == 0.0) {
+#pragma unroll
+    for (int j = 0; j < BB; ++j) dst[j] = 0;
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    double t = rint((double)v[j] / s + O);
+    c[j] = (int)fmin(fmax(t, 0.0), CMAX);
+  }
+  write_block<FMT>(dst, c, s16);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_pack_codes(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ sbits,
+    long long nblk, uint8_t *__restrict__ out) {
+  long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= nblk) return;
+  int c[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) c[j] = codes[i * 32 + j] & ((1 << FMT) - 1);
+  uint32_t sb = sbits[i];
+  if (FMT == RFPX_FP4) sb &= 0xFFu;
+  write_block<FMT>(out + i * blk_bytes(FMT), c, sb);
+}
+
+// Decode blocks whose code bytes sit every code_stride bytes and whose
+// scale bytes sit every scale_stride bytes: canonical blocks (both strides
+// the block size) or the two planes of the device image.
+__global__ __launch_bounds__(kThreads) void k_unpack(
+    int fmt, const uint8_t *__restrict__ codes, int code_stride,
+    const uint8_t *__restrict__ scales, int scale_stride, long long nblk,
+    float *__restrict__ w) {
+  long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= nblk) return;
+  int cb = code_bytes(fmt);
+  uint8_t cbytes[17];
+  for (int j = 0; j < cb; ++j) cbytes[j] = codes[i * code_stride + j];
+  cbytes[cb] = 0;
+  const uint8_t *sp = scales + i * scale_stride;
+  double s;
+  if (fmt == RFPX_FP4)
+    s = ldexp(1.0, (int)sp[0] - 127);
+  else
+    s = (double)half_bits_to_float((uint32_t)(sp[0] | (sp[1] << 8)));
+  double o = (double)code_offset_f(fmt);
+  float *dst = w + i * 32;
+  for (int j = 0; j < 32; ++j)
+    dst[j] = (float)(((double)get_code(fmt, cbytes, j) - o) * s);
+}
+
+// Canonical blocks of one matrix -> its codes plane and scales plane.  The
+// first thread of the gate matrix of each expert also writes the expert's
+// table entry; expert 0 writes the image header.
+__global__ __launch_bounds__(kThreads) void k_image_matrix(
+    int fmt, const uint8_t *__restrict__ src, long long nblk,
+    uint8_t *__restrict__ image, uint64_t codes_off, uint64_t scales_off,
+    int write_desc, int expert, ExpertDesc desc, ImageHeader hdr) {
+  long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i == 0 && write_desc) {
+    ExpertDesc *t = reinterpret_cast<ExpertDesc *>(image + kImgTable) + expert;
+    *t = desc;
+    if (expert == 0) *reinterpret_cast<ImageHeader *>(image) = hdr;
+  }
+  if (i >= nblk) return;
+  int cb = code_bytes(fmt), sb = scale_bytes(fmt), bb = cb + sb;
+  const uint8_t *s = src + i * bb;
+  uint8_t *c = image + codes_off + i * cb;
+  uint8_t *sc = image + scales_off + i * sb;
+  for (int j = 0; j < cb; ++j) c[j] = s[j];
+  for (int j = 0; j < sb; ++j) sc[j] = s[cb + j];
+}
+
+unsigned grid_for(long long n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+rfpx_status check_matrix(int fmt, int rows, int cols) {
+  if (!valid_fmt(fmt)) return fail(RFPX_E_FORMAT, "unknown format %d", fmt);
+  if (rows < 0 || cols < 0 || cols % 32)
+    return fail(RFPX_E_SHAPE, "matrix %dx%d: cols must be a multiple of 32",
+                rows, cols);
+  return RFPX_OK;
+}
+
+}  // namespace
+}  // namespace rfpx
+
+using namespace rfpx;
+
+extern "C" {
+
+size_t rfpx_block_bytes(int fmt) {
+  return valid_fmt(fmt) ? (size_t)blk_bytes(fmt) : 0;
+}
+
+size_t rfpx_matrix_bytes(int fmt, int rows, int cols) {
+  if (!valid_fmt(fmt) || rows < 0 || cols < 0 || cols % 32) return 0;
+  return (size_t)rows * (size_t)(cols / 32) * (size_t)blk_bytes(fmt);
+}
+
+rfpx_status rfpx_pack(int fmt, const float *w, int rows, int cols, uint8_t *out,
+                      size_t cap, void *stream) {
+  rfpx_status st = check_matrix(fmt, rows, cols);
+  if (st) return st;
+  long long nblk = (long long)rows * (cols / 32);
+  if (nblk == 0) return RFPX_OK;
+  if (!w || !out) return fail(RFPX_E_ARG, "rfpx_pack: null pointer");
+  if (cap < rfpx_matrix_bytes(fmt, rows, cols))
+    return fail(RFPX_E_WORKSPACE, "rfpx_pack: output holds %zu bytes, needs %zu",
+                cap, rfpx_matrix_bytes(fmt, rows, cols));
+  hipStream_t s = (hipStream_t)stream;
+  switch (fmt) {
+    case RFPX_FP2: k_pack<RFPX_FP2><<<grid_for(nblk), kThreads, 0, s>>>(w, nblk, out); break;
+    case RFPX_FP3: k_pack<RFPX_FP3><<<grid_for(nblk), kThreads, 0, s>>>(w, nblk, out); break;
+    default: k_pack<RFPX_FP4><<<grid_for(nblk), kThreads, 0, s>>>(w, nblk, out); break;
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "rfpx_pack: %s", hipGetErrorString(e));
+}
+
+rfpx_status rfpx_pack_codes(int fmt, const uint8_t *codes, const uint16_t *sbits,
+                            int rows, int cols, uint8_t *out, size_t cap,
+                            void *stream) {
+  rfpx_status st = check_matrix(fmt, rows, cols);
+  if (st) return st;
+  long long nblk = (long long)rows * (cols / 32);
+  if (nblk == 0) return RFPX_OK;
+  if (!codes || !sbits || !out) return fail(RFPX_E_ARG, "rfpx_pack_codes: null pointer");
+  if (cap < rfpx_matrix_bytes(fmt, rows, cols))
+    return fail(RFPX_E_WORKSPACE, "rfpx_pack_codes: output too small");
+  hipStream_t s = (hipStream_t)stream;
+  switch (fmt) {
+    case RFPX_FP2: k_pack_codes<RFPX_FP2><<<grid_for(nblk), kThreads, 0, s>>>(codes, sbits, nblk, out); break;
+    case RFPX_FP3: k_pack_codes<RFPX_FP3><<<grid_for(nblk), kThreads, 0, s>>>(codes, sbits, nblk, out); break;
+    default: k_pack_codes<RFPX_FP4><<<grid_for(nblk), kThreads, 0, s>>>(codes, sbits, nblk, out); break;
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "rfpx_pack_codes: %s", hipGetErrorString(e));
+}
+
+rfpx_status rfpx_unpack(int fmt, const uint8_t *in, int rows, int cols, float *w,
+                        void *stream) {
+  rfpx_status st = check_matrix(fmt, rows, cols);
+  if (st) return st;
+  long long nblk = (long long)rows * (cols / 32);
+  if (nblk == 0) return RFPX_OK;
+  if (!in || !w) return fail(RFPX_E_ARG, "rfpx_unpack: null pointer");
+  int bb = blk_bytes(fmt), cb = code_bytes(fmt);
+  k_unpack<<<grid_for(nblk), kThreads, 0, (hipStream_t)stream>>>(fmt, in, bb, in + cb, bb,
+                                                                 nblk, w);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "rfpx_unpack: %s", hipGetErrorString(e));
+}
+
+size_t moe_image_bytes(int d, int f, int n_experts, const int *fmts) {
+  if (!fmts || d <= 0 || f <= 0 || d % 32 || f % 32 || n_experts < 1 ||
+      n_experts > kEMax)
+    return 0;
+  for (int i = 0; i < 3 * (n_experts + 1); ++i)
+    if (!valid_fmt(fmts[i])) return 0;
+  return image_layout(d, f, n_experts, fmts, nullptr);
+}
+
+rfpx_status moe_image_build(int d, int f, int n_experts, const int *fmts,
+                            const uint8_t *const *canonical, uint8_t *image,
+                            size_t cap, void *stream) {
+  if (!fmts || !canonical || !image) return fail(RFPX_E_ARG, "moe_image_build: null pointer");
+  size_t need = moe_image_bytes(d, f, n_experts, fmts);
+  if (!need) return fail(RFPX_E_SHAPE, "moe_image_build: bad d=%d f=%d E=%d or format table", d, f, n_experts);
+  if ((uintptr_t)image % 256) return fail(RFPX_E_ALIGN, "moe_image_build: image not 256-byte aligned");
+  if (cap < need) return fail(RFPX_E_WORKSPACE, "moe_image_build: image holds %zu bytes, needs %zu", cap, need);
+  for (int e = 0; e <= n_experts; ++e)
+    if (fmts[3 * e] != fmts[3 * e + 1])
+      return fail(RFPX_E_FORMAT, "moe_image_build: expert %d gate/up formats differ", e);
+  for (int i = 0; i < 3 * (n_experts + 1); ++i)
+    if (!canonical[i]) return fail(RFPX_E_ARG, "moe_image_build: canonical[%d] is null", i);
+  ExpertDesc *desc = new ExpertDesc[n_experts + 1];
+  image_layout(d, f, n_experts, fmts, desc);
+  ImageHeader hdr{};
+  hdr.magic = kMagic;
+  hdr.version = kVersion;
+  hdr.d = d;
+  hdr.f = f;
+  hdr.E = n_experts;
+  hdr.total = need;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = hipSuccess;
+  for (int e = 0; e <= n_experts && err == hipSuccess; ++e) {
+    for (int m = 0; m < 3; ++m) {
+      int fmt = fmts[3 * e + m];
+      int rows = m < 2 ? f : d, cols = m < 2 ? d : f;
+      long long nblk = (long long)rows * (cols / 32);
+      k_image_matrix<<<grid_for(nblk), kThreads, 0, s>>>(
+          fmt, canonical[3 * e + m], nblk, image, desc[e].codes[m],
+          desc[e].scales[m], m == 0, e, desc[e], hdr);
+      err = hipGetLastError();
+      if (err != hipSuccess) break;
+    }
+  }
+  delete[] desc;
+  return err == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_image_build: %s", hipGetErrorString(err));
+}
+
+rfpx_status moe_image_unpack(const moe_layer *L, int expert, int matrix, float *w,
+                             void *stream) {
+  if (!L || !L->fmts || !L->image || !w) return fail(RFPX_E_ARG, "moe_image_unpack: null pointer");
+  if (expert < 0 || expert > L->n_experts || matrix < 0 || matrix > 2)
+    return fail(RFPX_E_ARG, "moe_image_unpack: expert %d matrix %d out of range", expert, matrix);
+  if (!moe_image_bytes(L->d, L->f, L->n_experts, L->fmts))
+    return fail(RFPX_E_SHAPE, "moe_image_unpack: bad layer shape or format table");
+  ExpertDesc *desc = new ExpertDesc[L->n_experts + 1];
+  image_layout(L->d, L->f, L->n_experts, L->fmts, desc);
+  int fmt = L->fmts[3 * expert + matrix];
+  int rows = matrix < 2 ? L->f : L->d, cols = matrix < 2 ? L->d : L->f;
+  long long nblk = (long long)rows * (cols / 32);
+  k_unpack<<<grid_for(nblk), kThreads, 0, (hipStream_t)stream>>>(
+      fmt, L->image + desc[expert].codes[matrix], code_bytes(fmt),
+      L->image + desc[expert].scales[matrix], scale_bytes(fmt), nblk, w);
+  delete[] desc;
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_image_unpack: %s", hipGetErrorString(e));
+}
+
+}  // extern "C"

@@ -1,0 +1,198 @@
+/*
+ * rfpx.h -- C ABI of librfpx: one routed-MoE layer over block-quantized
+ * experts on an AMD MI355X (gfx950), decode (q = 1..8 verify columns) and a
+ * prefill chunk.
+ *
+ * Pages cited below:
+ *   [P2] "APU 实现 token 自由：AMD Ryzen AI MAX+ 395 跑 DeepSeek V4 Flash，284B
+ *        模型跑出 32 tok/s" (ainomam.com), section "Lucebox 的优化三板斧".
+ *   [P3] "DeepSeek V4 Flash 在 128GB 锐龙 AI MAX+ 上跑到 32 tok/s"
+ *        (taozi.news), sections "ROCmFPX：把 284B 权重压进 128 GB",
+ *        "解码：32 tok/s" and "稀疏预填充：约 250 tok/s".
+ *   [P5] "Lucebox专攻DeepSeek V4：DSpark草稿模型、MoE专家并行与ROCmFPX量化达成
+ *        42 tok/s" (m.mzlw.cn), sections "MoE 专家并行" and "ROCmFPX 量化".
+ *
+ * ---------------------------------------------------------------- formats
+ * [P3] "ROCmFPX": a family of block formats, each block holding the low-bit
+ * codes of 32 weights and a scale; ROCmFP2 takes 10 bytes per block (2.50
+ * bit/weight), ROCmFP3 about 3.50 bit/weight, ROCmFP4 ("fast path") about
+ * 4.25 bit/weight.  The pages stop at block size; this library fixes the bit
+ * layout of one canonical block as:
+ *
+ *   FP2, 10 B: bytes 0..7 = 32 2-bit codes, code j in bits 2(j%4)..2(j%4)+1
+ *              of byte j/4; bytes 8..9 = IEEE fp16 scale s, little-endian.
+ *              w_j = (code_j - 1.5) * s          codebook {-1.5,-0.5,0.5,1.5}
+ *   FP3, 14 B: bytes 0..11 = one little-endian 96-bit integer, code j in its
+ *              bits 3j..3j+2 (codes 10 and 21 straddle bytes); bytes 12..13 =
+ *              fp16 scale s.   w_j = (code_j - 3.5) * s
+ *   FP4, 17 B: bytes 0..15 = 32 4-bit codes, code j in the low nibble of byte
+ *              j/2 for even j, the high nibble for odd j; byte 16 = E8M0
+ *              exponent e.     w_j = (code_j - 7.5) * 2^(e-127)
+ *
+ * A row-major matrix of R rows and C columns (C a multiple of 32) is R*C/32
+ * canonical blocks, block b of row r covering columns 32b..32b+31.  Every
+ * dequantized weight is exact in fp32.
+ *
+ * [P3] "ROCmFPX" and [P2]: routed gate and up use FP2, routed down FP3,
+ * dense or sensitive projections FP4 or wider; [P5] "ROCmFPX 量化": the width
+ * may also be chosen per expert by routing hotness.  The library accepts any
+ * of the three formats for any matrix, with gate and up of one expert in the
+ * same format.
+ *
+ * ------------------------------------------------------------ the layer
+ * [P5] "MoE 专家并行": each layer routes to 6 of 256 experts and adds 1
+ * shared expert.  For every column c of x[q][d]:
+ *   s[c][e]  = sum_i Wr[e][i] * x[c][i]                     (router, fp32)
+ *   ids[c]   = the k experts of largest score, score descending, ties to the
+ *              lower index                                    (TOP-K/ARGSORT, [P2])
+ *   w[c][j]  = routed_scale * softmax over the k selected scores
+ *   o_e      = Down_e ( silu(Gate_e x_c) * (Up_e x_c) )      (SiLU-gated FFN)
+ *   y[c]     = sum_j w[c][j] * o_ids[c][j]  +  o_shared
+ * Decode (q columns, [P3] "解码"): each packed block an expert needs is read
+ * and decoded once per call and applied to every column that selected that
+ * expert ([P2]: in the q=4 verify path each packed weight is decoded once
+ * for all 4 columns).  Arithmetic is fp32 with exact weights and exact
+ * activations; results differ from an exact evaluation only by fp32
+ * summation order.
+ *
+ * ------------------------------------------------------------ conventions
+ * - Every pointer named *_dev, and every pointer inside moe_layer except
+ *   fmts, is device memory of the current HIP device, allocated and freed by
+ *   the caller.  Host pointers are named *_host.
+ * - The library never allocates or frees device memory, keeps no state
+ *   between calls and never synchronizes the stream, except where a function
+ *   says so.  Work is enqueued on `stream` (a hipStream_t; NULL = default).
+ * - Every function validates its arguments on the host before enqueueing
+ *   anything and returns an rfpx_status; nothing is launched on error.
+ *   rfpx_last_error() then gives a message (thread-local).  A failed kernel
+ *   launch returns RFPX_E_HIP.  Faults inside kernels surface at the caller's
+ *   next synchronization.
+ * - Calls that share a workspace must not overlap in time; calls with
+ *   separate workspaces may run concurrently.
+ */
+#ifndef RFPX_H
+#define RFPX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RFPX_FP2 = 2, RFPX_FP3 = 3, RFPX_FP4 = 4 } rfpx_fmt;
+typedef enum { RFPX_X_F32 = 0, RFPX_X_BF16 = 1 } rfpx_xtype;
+typedef enum {
+  RFPX_OK = 0,
+  RFPX_E_ARG = -1,       /* null pointer, bad enum, bad count */
+  RFPX_E_SHAPE = -2,     /* unsupported d, f, E, k, q or T */
+  RFPX_E_ALIGN = -3,     /* pointer not aligned as required */
+  RFPX_E_FORMAT = -4,    /* bad format table or image header */
+  RFPX_E_WORKSPACE = -5, /* workspace or output capacity too small */
+  RFPX_E_HIP = -6        /* a HIP call failed */
+} rfpx_status;
+
+/* Limits of this build. */
+#define RFPX_Q_MAX 8    /* verify columns per decode call */
+#define RFPX_K_MAX 8    /* routed experts per column */
+#define RFPX_E_MAX 1024 /* routed experts per layer */
+
+/* Bytes of one canonical block: 10, 14, 17; 0 for an unknown format. */
+size_t rfpx_block_bytes(int fmt);
+/* rows * cols/32 * block bytes; 0 if cols is not a multiple of 32. */
+size_t rfpx_matrix_bytes(int fmt, int rows, int cols);
+
+/* Quantize w_dev[rows][cols] (fp32, finite) into canonical blocks at
+ * out_dev (capacity cap bytes).  Per block: a = max|w|; FP2/FP3 scale s =
+ * fp16 nearest-even of a/1.5 (a/3.5), 65504 on overflow, and if s rounds to
+ * 0 (or a = 0) the block is all-zero bytes; codes = nearest-even integer of
+ * w/s + offset, clamped.  FP4: e = clamp(127 + ceil(log2(a/7.5)), 1, 254),
+ * codes = nearest-even of w*2^(127-e) + 7.5, clamped; a = 0 gives all-zero
+ * bytes.  Divisions and roundings are done in double on the device.
+ * Requires cols % 32 == 0, rows >= 0. */
+rfpx_status rfpx_pack(int fmt, const float *w_dev, int rows, int cols,
+                      uint8_t *out_dev, size_t cap, void *stream);
+/* Bit-pack codes_dev[rows][cols] (one code per byte, only the low 2/3/4
+ * bits are used) and scale_bits_dev[rows][cols/32] (fp16 bit patterns for
+ * FP2/FP3, E8M0 in the low byte for FP4) into canonical blocks. */
+rfpx_status rfpx_pack_codes(int fmt, const uint8_t *codes_dev,
+                            const uint16_t *scale_bits_dev, int rows, int cols,
+                            uint8_t *out_dev, size_t cap, void *stream);
+/* Dequantize canonical blocks into w_dev[rows][cols] fp32 (exact). */
+rfpx_status rfpx_unpack(int fmt, const uint8_t *in_dev, int rows, int cols,
+                        float *w_dev, void *stream);
+
+/* ------------------------------------------------------- device image
+ * The layer's experts live in one device buffer, the image:
+ *   header (64 B) | expert table (E+1) x 64 B | planes
+ * Experts are stored expert-major (0..E-1 routed, E = shared).  Each matrix
+ * (gate f x d, up f x d, down d x f) is split into a codes plane (rows x
+ * cols/32 x 8|12|16 bytes, row-major) and a scales plane (rows x cols/32 x
+ * 2|1 bytes); every plane starts on a 256-byte boundary.  The byte count of
+ * the planes equals the canonical byte count: the image is a permutation of
+ * the canonical blocks plus the header, table and alignment gaps. */
+size_t moe_image_bytes(int d, int f, int n_experts, const int *fmts_host);
+
+/* Build the image from canonical matrices.  fmts_host[3*e + m] is the format
+ * of matrix m (0 gate, 1 up, 2 down) of expert e, e = 0..n_experts (the last
+ * is the shared expert); canonical_host[3*e + m] is a host array of device
+ * pointers to those canonical matrices.  image_dev must be 256-byte aligned
+ * and hold moe_image_bytes().  Gate and up of an expert must share a format.
+ * Enqueues one copy kernel per matrix; the canonical buffers may be freed
+ * once the stream has passed this call. */
+rfpx_status moe_image_build(int d, int f, int n_experts, const int *fmts_host,
+                            const uint8_t *const *canonical_host,
+                            uint8_t *image_dev, size_t cap, void *stream);
+
+typedef struct {
+  int d;              /* model width, a power of two from 256 to 16384 */
+  int f;              /* expert width, a power of two from 64 to 8192 */
+  int n_experts;      /* routed experts E, 1..RFPX_E_MAX */
+  int top_k;          /* k, 1..min(E, RFPX_K_MAX) */
+  float routed_scale; /* multiplies the k gating weights (1.0) */
+  const float *router_w;  /* device, [E][d] fp32 */
+  const uint8_t *image;   /* device, built by moe_image_build for fmts */
+  const int *fmts;        /* host, [(E+1)*3], the table the image was built with */
+} moe_layer;
+
+/* Dequantize matrix m of expert e straight from the image into w_dev
+ * (rows x cols fp32) -- a check of the image layout. */
+rfpx_status moe_image_unpack(const moe_layer *L, int expert, int matrix,
+                             float *w_dev, void *stream);
+
+/* Workspace for moe_route_topk / moe_layer_forward with q columns
+ * (prefill = 0), or for moe_prefill_forward with T tokens (prefill = 1);
+ * 0 if the shape is unsupported.  The workspace must be 256-byte aligned and
+ * zero-filled before its first use; every call leaves its counters at zero
+ * again, so it is then reusable without clearing. */
+size_t moe_workspace_bytes(const moe_layer *L, int q_or_T, int prefill);
+
+/* Router scores, top-k and gating for q columns of x_dev ([q][d] fp32 or
+ * bf16 per xtype): ids_dev[q][k] int32 (score descending, ties to the lower
+ * index) and w_dev[q][k] fp32. */
+rfpx_status moe_route_topk(const moe_layer *L, const void *x_dev, int xtype,
+                           int q, int32_t *ids_dev, float *w_dev, void *ws_dev,
+                           size_t ws_bytes, void *stream);
+
+/* One decode step of the layer for q = 1..RFPX_Q_MAX columns: y_dev[q][d]
+ * fp32.  Each column is routed independently; each expert block is read
+ * once and applied to all columns that chose the expert. */
+rfpx_status moe_layer_forward(const moe_layer *L, const void *x_dev, int xtype,
+                              int q, float *y_dev, void *ws_dev,
+                              size_t ws_bytes, void *stream);
+
+/* One prefill chunk of T tokens (x_dev [T][d] bf16 or fp32): tokens are
+ * grouped by expert and each expert runs as a dense grouped product on the
+ * matrix cores.  y_dev[T][d] fp32.  ([P3] "稀疏预填充": prefill is batched per
+ * layer.) */
+rfpx_status moe_prefill_forward(const moe_layer *L, const void *x_dev,
+                                int xtype, int T, float *y_dev, void *ws_dev,
+                                size_t ws_bytes, void *stream);
+
+const char *rfpx_status_str(int status);
+const char *rfpx_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RFPX_H */

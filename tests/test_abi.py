@@ -1,0 +1,171 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/rfpx.h declares, and rejects bad arguments before launching
+anything (these calls never reach the GPU, so they run without one)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_quantized_expert_amd as bqe
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rfpx.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rfpx_\w+|moe_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bqe.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return bqe.lib()
+
+
+def test_exports_every_declared_function(lib):
+    declared = header_functions()
+    assert len(declared) == 14
+    assert set(declared) == set(bqe.SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_block_and_matrix_bytes(lib):
+    assert [lib.rfpx_block_bytes(f) for f in (2, 3, 4)] == [10, 14, 17]
+    assert lib.rfpx_block_bytes(5) == 0
+    assert lib.rfpx_matrix_bytes(2, 2048, 4096) == 2048 * 128 * 10 == 2621440
+    assert lib.rfpx_matrix_bytes(3, 4096, 2048) == 3670016
+    assert lib.rfpx_matrix_bytes(4, 2048, 4096) == 4456448
+    assert lib.rfpx_matrix_bytes(2, 4, 33) == 0
+
+
+def _fmts(E, hot=()):
+    f = np.empty((E + 1, 3), np.int32)
+    f[:, :2], f[:, 2] = 2, 3
+    for e in hot:
+        f[e] = 4
+    f[E] = 4
+    return f
+
+
+def test_image_bytes_equal_canonical_plus_header(lib):
+    # decode-size layer: every plane is a multiple of 256 bytes, so the image
+    # is the canonical bytes plus the header and the expert table
+    E, d, f = 256, 4096, 2048
+    fm = _fmts(E)
+    n = bqe.moe_image_bytes(d, f, E, fm)
+    canonical = 256 * (2 * 2621440 + 3670016) + 3 * 4456448 - 4456448 + 2 * 4456448
+    canonical = 256 * 8912896 + 13369344
+    assert canonical == 2295070720
+    table = (64 + 257 * 64 + 255) // 256 * 256
+    assert n == canonical + table
+    # hot experts in FP4 (the q=5 mixed layer): 32 * (13369344 - 8912896) more
+    n4 = bqe.moe_image_bytes(d, f, E, _fmts(E, hot=range(32)))
+    assert n4 - table == 2295070720 + 32 * (13369344 - 8912896) == 2437677056
+
+
+def test_image_bytes_rejects_bad_tables(lib):
+    fm = _fmts(8)
+    fm[3, 1] = 7
+    assert bqe.moe_image_bytes(256, 128, 8, fm) == 0
+    assert bqe.moe_image_bytes(256, 100, 8, _fmts(8)) == 0
+
+
+class _Dummy:
+    """Stand-ins for device tensors: only data_ptr() is read, and every
+    call below fails validation before anything dereferences it."""
+
+    def __init__(self, ptr):
+        self._p = ptr
+        self.is_cuda = True
+
+    def data_ptr(self):
+        return self._p
+
+    def is_contiguous(self):
+        return True
+
+
+def _layer(d=256, f=128, E=8, k=2, fmts=None, image=4096, wr=8192):
+    fm = _fmts(E) if fmts is None else fmts
+    return bqe.MoeLayer(d, f, E, k, _Dummy(wr), _Dummy(image), fm)
+
+
+def _fwd(lib, L, x=0x10000, xtype=0, q=1, y=0x20000, ws=0x30000, nbytes=1 << 30):
+    return lib.moe_layer_forward(L.ref, C.c_void_p(x), xtype, q, C.c_void_p(y),
+                                 C.c_void_p(ws), nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=300), -2), (dict(d=8192), -2), (dict(f=48), -2), (dict(E=0), -2),
+    (dict(k=9), -2), (dict(E=4, k=5), -2),
+])
+def test_forward_rejects_shapes(lib, kw, status):
+    E = kw.pop("E", 8)
+    fm = _fmts(max(E, 1))[: E + 1] if E > 0 else _fmts(1)[:1]
+    L = _layer(E=E, fmts=fm, **kw)
+    assert _fwd(lib, L) == status
+    assert lib.rfpx_last_error()
+
+
+def test_forward_rejects_arguments(lib):
+    L = _layer()
+    assert _fwd(lib, L, q=0) == -2
+    assert _fwd(lib, L, q=9) == -2
+    assert _fwd(lib, L, xtype=3) == -1
+    assert _fwd(lib, L, x=0) == -1
+    assert _fwd(lib, L, y=0) == -1
+    assert _fwd(lib, L, ws=0) == -1
+    assert _fwd(lib, L, ws=0x30010) == -3          # misaligned workspace
+    assert _fwd(lib, L, x=0x10004) == -3           # misaligned x
+    assert _fwd(lib, _layer(image=4096 + 64)) == -3
+    assert _fwd(lib, L, nbytes=16) == -5
+    assert b"workspace" in lib.rfpx_last_error()
+    fm = _fmts(8)
+    fm[2, 1] = 4  # gate FP2, up FP4
+    assert _fwd(lib, _layer(fmts=fm)) == -4
+    fm = _fmts(8)
+    fm[5, 2] = 9
+    assert _fwd(lib, _layer(fmts=fm)) == -4
+
+
+def test_workspace_bytes_shapes(lib):
+    L = _layer()
+    n1 = bqe.moe_workspace_bytes(L, 1)
+    n4 = bqe.moe_workspace_bytes(L, 4)
+    assert 0 < n1 < n4
+    assert bqe.moe_workspace_bytes(L, 9) == 0
+    assert bqe.moe_workspace_bytes(_layer(d=4096, f=2048, E=256, k=6,
+                                          fmts=_fmts(256)), 5) > 0
+
+
+def test_codec_rejects_bad_arguments(lib):
+    p = C.c_void_p(0x1000)
+    assert lib.rfpx_pack(5, p, 4, 64, p, 1 << 20, None) == -4
+    assert lib.rfpx_pack(2, p, 4, 33, p, 1 << 20, None) == -2
+    assert lib.rfpx_pack(2, p, 4, 64, p, 10, None) == -5
+    assert lib.rfpx_pack(2, None, 4, 64, p, 1 << 20, None) == -1
+    assert lib.rfpx_pack(2, p, 0, 64, p, 0, None) == 0  # empty matrix: nothing to do
+    assert lib.rfpx_unpack(3, None, 4, 64, p, None) == -1
+    assert lib.rfpx_pack_codes(4, p, None, 4, 64, p, 1 << 20, None) == -1
+
+
+def test_status_strings(lib):
+    assert lib.rfpx_status_str(0) == b"ok"
+    assert lib.rfpx_status_str(-5).startswith(b"workspace")
+    assert lib.rfpx_status_str(42) == b"unknown status"
+
+
+def test_generator_layer_shapes_match_library(lib):
+    lay = synth.gen_layer(synth.CONFIGS[1], 0, threads=2)
+    for e in range(lay.E + 1):
+        for m in range(3):
+            rows, cols = lay.matrix_shape(m)
+            assert lay.mat(e, m).size == lib.rfpx_matrix_bytes(int(lay.fmts[e][m]), rows, cols)

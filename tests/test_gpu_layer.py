@@ -1,0 +1,170 @@
+"""GPU layer parity: moe_layer_forward against the CPU oracle on the decode
+workloads (max|dy| <= 2e-3 * RMS(y)), plus q-batching, determinism, mixed
+formats and edge shapes."""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import assert_close, rel_err, to_device_x
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bqe():
+    import block_quantized_expert_amd as m
+    m.lib()
+    return m
+
+
+def _run(bqe, L, x_np):
+    import torch
+    y = bqe.moe_layer_forward(L, to_device_x(x_np))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def _oracle(lay, x_np, xtype):
+    return oracle.layer_forward_synth(lay, x_np, xtype)
+
+
+# ------------------------------------------------------------- tiny (cfg 1)
+
+@pytest.fixture(scope="module")
+def tiny(bqe):
+    cfg = synth.CONFIGS[1]
+    lay = synth.gen_layer(cfg, 0, threads=4)
+    return cfg, lay, bqe.upload_layer(lay)
+
+
+def test_tiny_four_tokens_q1(bqe, tiny):
+    cfg, lay, L = tiny
+    cols = synth.gen_columns(cfg, lay, 4)
+    y_ref, _, _ = _oracle(lay, cols.x, "f32")
+    for c in range(4):
+        y = _run(bqe, L, cols.x[c:c + 1])
+        assert_close(y, y_ref[c:c + 1], what=f"token {c}")
+
+
+def test_tiny_q4_matches_q1(bqe, tiny):
+    cfg, lay, L = tiny
+    cols = synth.gen_columns(cfg, lay, 4, variant=1)
+    y_ref, _, _ = _oracle(lay, cols.x, "f32")
+    y4 = _run(bqe, L, cols.x)
+    assert_close(y4, y_ref, what="q=4")
+    for c in range(4):
+        y1 = _run(bqe, L, cols.x[c:c + 1])
+        assert rel_err(y4[c], y1[0]) <= 1e-5
+
+
+def test_tiny_all_columns_identical(bqe, tiny):
+    # every expert is chosen by all q columns: exercises passes of two
+    # columns plus an odd remainder
+    cfg, lay, L = tiny
+    cols = synth.gen_columns(cfg, lay, 1, variant=2)
+    for q in (2, 3, 5, 8):
+        x = np.repeat(cols.x, q, axis=0)
+        y = _run(bqe, L, x)
+        y_ref, _, _ = _oracle(lay, x, "f32")
+        assert_close(y, y_ref, what=f"q={q}")
+
+
+def test_tiny_deterministic(bqe, tiny):
+    cfg, lay, L = tiny
+    cols = synth.gen_columns(cfg, lay, 3, variant=3)
+    a, b = _run(bqe, L, cols.x), _run(bqe, L, cols.x)
+    assert np.array_equal(a, b)
+
+
+def test_tiny_bf16_activations(bqe, tiny):
+    cfg, lay, L = tiny
+    cfg16 = synth.Config(**{**cfg.__dict__, "xtype": "bf16"})
+    cols = synth.gen_columns(cfg16, lay, 4, variant=4)
+    y_ref, _, _ = _oracle(lay, cols.x, "bf16")
+    assert_close(_run(bqe, L, cols.x), y_ref, what="bf16 x")
+
+
+# ------------------------------------------------------- mixed small shapes
+
+@pytest.mark.parametrize("d,f,E,k,seed", [(512, 256, 16, 4, 1), (1024, 64, 32, 8, 2),
+                                           (256, 1024, 12, 3, 3), (4096, 128, 8, 2, 4)])
+def test_mixed_formats_and_shapes(bqe, d, f, E, k, seed):
+    """Every format in every matrix position (gate/up FP3, down FP2, ...)."""
+    cfg = synth.Config(0, "t", d, f, E, k, 1, "f32", "natural", scale_floor=1e-3,
+                       master=100 + seed)
+    lay = synth.gen_layer(cfg, 0, threads=4)
+    # rewrite the format table: cycle formats, regenerate those matrices
+    rng = np.random.default_rng(seed)
+    fm = lay.fmts.copy()
+    for e in range(E + 1):
+        g = [2, 3, 4][(e + seed) % 3]
+        fm[e] = [g, g, [2, 3, 4][(e + 2 * seed) % 3]]
+    mats = []
+    for e in range(E + 1):
+        for m in range(3):
+            rows, cols = (f, d) if m < 2 else (d, f)
+            mats.append(synth.random_matrix(int(rng.integers(1 << 30)), int(fm[e][m]),
+                                            rows, cols, 0.05, 1e-3))
+    sizes = [m.size for m in mats]
+    lay.fmts = fm
+    lay.offsets = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.int64)
+    lay.blob = np.concatenate(mats)
+    L = bqe.upload_layer(lay)
+    for xt in ("f32", "bf16"):
+        for q in (1, 3):
+            c2 = synth.Config(**{**cfg.__dict__, "xtype": xt})
+            cols = synth.gen_columns(c2, lay, q, variant=q)
+            y_ref, _, _ = _oracle(lay, cols.x, xt)
+            assert_close(_run(bqe, L, cols.x), y_ref, what=f"{xt} q={q}")
+
+
+# ------------------------------------------------------ decode size (2, 3)
+
+@pytest.fixture(scope="module")
+def decode_layer(bqe):
+    import torch
+    cfg = synth.CONFIGS[2]
+    lay = synth.gen_layer(cfg, 0)
+    L = bqe.upload_layer(lay)
+    yield cfg, lay, L
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_decode_q1(bqe, decode_layer):
+    cfg, lay, L = decode_layer
+    cols = synth.gen_columns(cfg, lay, 3)
+    with cf.ThreadPoolExecutor(3) as ex:
+        refs = list(ex.map(lambda c: _oracle(lay, cols.x[c:c + 1], "bf16")[0], range(3)))
+    for c in range(3):
+        assert_close(_run(bqe, L, cols.x[c:c + 1]), refs[c], what=f"column {c}")
+
+
+def test_verify_q4_zipf(bqe, decode_layer):
+    cfg2, lay, L = decode_layer
+    cfg = synth.CONFIGS[3]
+    cols = synth.gen_columns(cfg, lay, 4)
+    with cf.ThreadPoolExecutor(4) as ex:
+        refs = list(ex.map(lambda c: _oracle(lay, cols.x[c:c + 1], "bf16")[0], range(4)))
+    y_ref = np.concatenate(refs)
+    assert_close(_run(bqe, L, cols.x), y_ref, what="q=4")
+
+
+# ------------------------------------------------------ q=5 mixed (cfg 4)
+
+@pytest.mark.parametrize("layer", [0, 21, 42])
+def test_verify_q5_hot_fp4(bqe, layer):
+    import torch
+    cfg = synth.CONFIGS[4]
+    lay = synth.gen_layer(cfg, layer)
+    L = bqe.upload_layer(lay)
+    cols = synth.gen_columns(cfg, lay, 5, layer=layer)
+    y = _run(bqe, L, cols.x)
+    with cf.ThreadPoolExecutor(5) as ex:
+        refs = list(ex.map(lambda c: _oracle(lay, cols.x[c:c + 1], "bf16")[0], range(5)))
+    assert_close(y, np.concatenate(refs), what=f"layer {layer}")
+    del L
+    torch.cuda.empty_cache()
