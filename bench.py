@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of one routed-MoE layer over block-quantized experts on MI355X.
+
+Metric: MoE-layer decode tokens/s (verify columns per second through one
+layer) and the packed expert bytes streamed per step as HBM GB/s.
+
+Workloads (synthetic, seeded; shapes of DeepSeek-V4-Flash-class layers):
+  --config 2  (default) q=1 decode: d=4096, f=2048, 256 experts top-6 + 1
+              shared; gate/up FP2, down FP3, shared FP4; bf16 activations
+  --config 3  q=4 verify columns, Zipf(1.1) routing per column
+  --config 4  q=5 verify columns, Zipf(1.1), 32 hottest experts FP4, 43 layers
+A step is one moe_layer_forward call (router, top-k, batching, gate/up,
+down, combine) on one batch of q columns.  Steps rotate over --layers layer
+instances, each with its own router, experts and activations, so that no
+weight is re-read from the 256 MB last-level cache within a rotation.
+
+Timing: W warm-up steps, then K steps between two synchronizations, timed
+with events on the stream the kernels run on.  A second pass of K steps
+records a hipEvent between the three kernels of every step
+(moe_layer_forward_timed) to time the dominant kernel (gate/up) for the
+roofline entry.  The CPU oracle is timed on a bounded sample on the host.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer decode tokens/s and packed-weight HBM GB/s (% of peak) at q=1,4,5"
+HBM_PEAK_GBS = 8000.0
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        self.lib = C.CDLL(path)
+        self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self, n):
+        arr = (C.c_void_p * n)()
+        for i in range(n):
+            h = C.c_void_p()
+            if self.lib.hipEventCreate(C.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = h
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = C.c_float()
+        if self.lib.hipEventElapsedTime(C.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, arr):
+        for h in arr:
+            self.lib.hipEventDestroy(h)
+
+
+def expert_bytes(lay, e):
+    import synth
+    tot = 0
+    gu = 0
+    for m in range(3):
+        rows, cols = lay.matrix_shape(m)
+        b = synth.matrix_bytes(int(lay.fmts[e][m]), rows, cols)
+        tot += b
+        if m < 2:
+            gu += b
+    return tot, gu
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4))
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer instances to rotate over (default 8; 43 for --config 4)")
+    ap.add_argument("--variants", type=int, default=4,
+                    help="activation batches per layer instance")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall time budget of the CPU oracle sample (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_quantized_expert_amd as bqe
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    n_layers = args.layers or (43 if args.config == 4 else 8)
+    q = cfg.q
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bqe.lib()
+
+    # ---- setup (untimed): images, activations, expected routing
+    t_setup = time.time()
+    layers, xs, step_bytes, step_gu = [], [], [], []
+    lay0 = None
+    x0_host = None
+    for l in range(n_layers):
+        lay = synth.gen_layer(cfg, l)
+        L = bqe.upload_layer(lay)
+        ws = bqe.workspace(L, q)
+        per = []
+        for v in range(args.variants):
+            cols = synth.gen_columns(cfg, lay, q, variant=v, layer=l)
+            x = torch.from_numpy(cols.x.view(np.int16)).view(torch.bfloat16).to(dev)
+            ids, _ = bqe.moe_route_topk(L, x, ws=ws)
+            ids = ids.cpu().numpy()
+            if cols.drawn is not None and not np.array_equal(ids, cols.drawn):
+                raise RuntimeError("routing differs from the prescribed expert sets")
+            uniq = sorted(set(int(e) for e in ids.reshape(-1)))
+            b = sum(expert_bytes(lay, e)[0] for e in uniq) + expert_bytes(lay, lay.E)[0]
+            g = sum(expert_bytes(lay, e)[1] for e in uniq) + expert_bytes(lay, lay.E)[1]
+            per.append((x, b, g, len(uniq)))
+            if l == 0 and v == 0:
+                x0_host = cols.x.copy()
+        layers.append((L, ws))
+        xs.append(per)
+        if l == 0:
+            lay0 = lay
+        else:
+            del lay
+        print(f"# layer {l + 1}/{n_layers} ready ({time.time() - t_setup:.1f}s)",
+              file=sys.stderr, flush=True)
+    y = torch.empty((q, cfg.d), dtype=torch.float32, device=dev)
+
+    order = [(s % n_layers, (s // n_layers) % args.variants) for s in range(args.steps)]
+    warm = [(s % n_layers, (s // n_layers) % args.variants) for s in range(args.warmup)]
+
+    def step(li, vi, events=None):
+        L, ws = layers[li]
+        x = xs[li][vi][0]
+        if events is None:
+            bqe.moe_layer_forward(L, x, y=y, ws=ws)
+        else:
+            bqe.moe_layer_forward_timed(L, x, y, ws, events)
+
+    for li, vi in warm:
+        step(li, vi)
+    torch.cuda.synchronize()
+
+    # ---- timed pass: whole steps
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for li, vi in order:
+        step(li, vi)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = q * args.steps / (total_ms / 1e3)
+    bytes_per_step = float(np.mean([xs[li][vi][1] for li, vi in order]))
+    gu_bytes = float(np.mean([xs[li][vi][2] for li, vi in order]))
+    uniq_mean = float(np.mean([xs[li][vi][3] for li, vi in order]))
+
+    # ---- timed pass: kernels of each step
+    he = HipEvents()
+    evs = [he.create(5) for _ in order]
+    torch.cuda.synchronize()
+    t0.record()
+    for (li, vi), ev in zip(order, evs):
+        step(li, vi, ev)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ev_ms = t0.elapsed_time(t1)
+    k_route = [he.elapsed_ms(ev[0], ev[1]) for ev in evs]
+    k_gu = [he.elapsed_ms(ev[1], ev[2]) for ev in evs]
+    k_dn = [he.elapsed_ms(ev[2], ev[3]) for ev in evs]
+    k_cb = [he.elapsed_ms(ev[3], ev[4]) for ev in evs]
+    for ev in evs:
+        he.destroy(ev)
+    gu_us = 1e3 * float(np.mean(k_gu))
+    gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        n_cols = 0
+        t = time.time()
+        while True:
+            oracle.layer_forward_synth(lay0, x0_host[:1], "bf16")
+            n_cols += 1
+            if time.time() - t >= args.cpu_seconds:
+                break
+        dt = time.time() - t
+        cpu = {"value": n_cols / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": (f"{n_cols} single-column decode steps of layer 0 (d={cfg.d}, "
+                          f"f={cfg.f}, E={cfg.E}, top-{cfg.k} + shared), plain C "
+                          f"oracle in double, single thread, {dt:.1f} s")}
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name, "config_id": cfg.cid, "q": q, "d": cfg.d,
+            "f": cfg.f, "experts": cfg.E, "top_k": cfg.k, "shared": 1,
+            "formats": ("gate/up FP2, down FP3, shared FP4"
+                        + (", 32 hottest experts FP4" if cfg.hot_fp4 else "")),
+            "activations": "bf16", "accumulate": "fp32",
+            "layers_rotated": n_layers, "activation_batches_per_layer": args.variants,
+            "graph_captured": False, "seed_master": cfg.master,
+        },
+        "step_hbm": {
+            "packed_expert_bytes_per_step": bytes_per_step,
+            "unique_routed_experts_per_step": uniq_mean,
+            "GB_per_s": bytes_per_step / (ms_per_step * 1e-3) / 1e9,
+            "frac_of_peak": bytes_per_step / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "router_bytes_per_step": cfg.E * cfg.d * 4,
+        },
+        "kernels_us": {
+            "route_topk": 1e3 * float(np.mean(k_route)),
+            "gate_up": gu_us,
+            "down": 1e3 * float(np.mean(k_dn)),
+            "combine": 1e3 * float(np.mean(k_cb)),
+            "step_with_events": total_ev_ms * 1e3 / args.steps,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_gateup (gate/up dequant-GEMV + SiLU, routed and shared)",
+            "achieved": gu_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gu_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": gu_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

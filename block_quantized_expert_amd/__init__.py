@@ -31,7 +31,8 @@ SYMBOLS = (
     "rfpx_block_bytes", "rfpx_matrix_bytes", "rfpx_pack", "rfpx_pack_codes",
     "rfpx_unpack", "moe_image_bytes", "moe_image_build", "moe_image_unpack",
     "moe_workspace_bytes", "moe_route_topk", "moe_layer_forward",
-    "moe_prefill_forward", "rfpx_status_str", "rfpx_last_error",
+    "moe_layer_forward_timed", "moe_prefill_forward", "rfpx_status_str",
+    "rfpx_last_error",
 )
 
 
@@ -86,6 +87,7 @@ def lib():
             "moe_workspace_bytes": (S, [LP, I, I]),
             "moe_route_topk": (I, [LP, P, I, I, P, P, P, S, P]),
             "moe_layer_forward": (I, [LP, P, I, I, P, P, S, P]),
+            "moe_layer_forward_timed": (I, [LP, P, I, I, P, P, S, P, P]),
             "moe_prefill_forward": (I, [LP, P, I, I, P, P, S, P]),
             "rfpx_status_str": (C.c_char_p, [I]),
             "rfpx_last_error": (C.c_char_p, []),
@@ -239,13 +241,13 @@ def moe_workspace_bytes(layer: MoeLayer, q_or_T: int, prefill: bool = False) -> 
 
 
 def workspace(layer: MoeLayer, q_or_T: int, prefill: bool = False):
-    """A zero-filled workspace of the right size (the library requires zeros
-    before first use and leaves them behind)."""
+    """A workspace of the right size (uninitialized: the library needs no
+    particular contents)."""
     import torch
     n = moe_workspace_bytes(layer, q_or_T, prefill)
     if n == 0:
         raise RfpxError("moe_workspace_bytes", -2, "unsupported shape")
-    return torch.zeros(n, dtype=torch.uint8, device=layer._image.device)
+    return torch.empty(n, dtype=torch.uint8, device=layer._image.device)
 
 
 def _xtype(x) -> int:
@@ -284,6 +286,16 @@ def moe_layer_forward(layer: MoeLayer, x, y=None, ws=None, stream=None):
     _check("moe_layer_forward", lib().moe_layer_forward(
         layer.ref, _ptr(x), _xtype(x), q, _ptr(y), _ptr(ws), ws.numel(),
         _stream(stream)))
+    return y
+
+
+def moe_layer_forward_timed(layer: MoeLayer, x, y, ws, events, stream=None):
+    """events: a ctypes array of 5 hipEvent_t handles (created by the
+    caller on this device), recorded around the four kernels."""
+    _need_cuda(x)
+    _check("moe_layer_forward_timed", lib().moe_layer_forward_timed(
+        layer.ref, _ptr(x), _xtype(x), x.shape[0], _ptr(y), _ptr(ws), ws.numel(),
+        _stream(stream), C.cast(events, C.c_void_p) if events is not None else None))
     return y
 
 

@@ -57,19 +57,31 @@ bool pow2_in(int v, int lo, int hi) {
   return v >= lo && v <= hi && (v & (v - 1)) == 0;
 }
 
-// Rows per workgroup tile for a set of formats: every format must fit in
-// 1..wmax waves of r rows (rpi rows per wave step), the tile must divide
-// `rows`, and (gate/up) hold whole 32-row blocks of h.
-bool pick_tile(const Geo *geo, unsigned fmts, int r, int wmax, int rows,
-               bool need32, int *rw) {
-  int lo = need32 ? 32 : 1, hi = rows;
+// Rows per workgroup tile.  A unit is r rows (rpi rows per wave step) of one
+// column part (tpl parts per row); the waves of a workgroup loop over the
+// tile's units.  Gate/up tiles hold whole 32-row blocks of h (the down
+// matrix's blocks); down tiles aim at one unit per wave.
+bool pick_tile_gateup(const Geo *geo, unsigned fmts, int r, int rows, int *rw) {
+  int t = 32;
+  for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
+    if ((fmts >> f) & 1u) t = t > geo[f].rpi * r ? t : geo[f].rpi * r;
+  if (t > rows || rows % t) return false;
+  *rw = t;
+  return true;
+}
+
+bool pick_tile_down(const Geo *geo, unsigned fmts, int r, int waves, int rows, int *rw) {
+  int lo = 1, hi = rows;
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f) {
     if (!((fmts >> f) & 1u)) continue;
-    lo = lo > geo[f].rpi * r ? lo : geo[f].rpi * r;
-    hi = hi < geo[f].rpi * r * wmax ? hi : geo[f].rpi * r * wmax;
+    const int unit = geo[f].rpi * r;
+    const int want = unit * waves / geo[f].tpl;
+    lo = lo > unit ? lo : unit;
+    hi = hi < want ? hi : want;
   }
-  if (hi < lo || rows % hi) return false;
-  *rw = hi;
+  const int t = hi > lo ? hi : lo;
+  if (t > rows || rows % t) return false;
+  *rw = t;
   return true;
 }
 
@@ -125,21 +137,18 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
     }
   }
   p->g = q == 1 ? 1 : 2;
-  p->r = 4;     // rows per wave: must match the kernels' R template
+  p->r = 4;     // rows per unit: must match the kernels' R template
   p->wmax = 8;  // waves per workgroup
-  if (!pick_tile(p->geo_gu, p->prep_fmts, p->r, p->wmax, L->f, true, &p->rw_gu))
+  if (!pick_tile_gateup(p->geo_gu, p->prep_fmts, p->r, L->f, &p->rw_gu))
     return fail(RFPX_E_SHAPE, "f=%d: no gate/up tile for this format mix", L->f);
-  if (!pick_tile(p->geo_dn, p->down_fmts, p->r, p->wmax, L->d, false, &p->rw_dn))
+  if (!pick_tile_down(p->geo_dn, p->down_fmts, p->r, p->wmax, L->d, &p->rw_dn))
     return fail(RFPX_E_SHAPE, "d=%d: no down tile for this format mix", L->d);
 
   WsLayout &w = p->wl;
   const int vx = xtype == RFPX_X_BF16 ? 1 : 2;
   const int nb_d = L->d / 32, nb_f = L->f / 32;
   w.max_slots = 1 + (q * L->top_k < L->n_experts ? q * L->top_k : L->n_experts);
-  w.n_tiles_down = L->d / p->rw_dn;
   size_t off = 0;
-  w.counters = off;
-  off = align_up(off + (size_t)(1 + w.n_tiles_down) * 4, 256);
   w.route = off;
   off = align_up(off + sizeof(RouteTable), 256);
   w.scores = off;
@@ -221,6 +230,12 @@ rfpx_status moe_route_topk(const moe_layer *L, const void *x, int xtype, int q,
 
 rfpx_status moe_layer_forward(const moe_layer *L, const void *x, int xtype, int q,
                               float *y, void *ws, size_t ws_bytes, void *stream) {
+  return moe_layer_forward_timed(L, x, xtype, q, y, ws, ws_bytes, stream, nullptr);
+}
+
+rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x, int xtype,
+                                    int q, float *y, void *ws, size_t ws_bytes,
+                                    void *stream, void *const *events) {
   ForwardPlan p;
   rfpx_status st = make_plan(L, q, xtype, &p);
   if (st) return st;
@@ -230,7 +245,11 @@ rfpx_status moe_layer_forward(const moe_layer *L, const void *x, int xtype, int 
   p.y = y;
   p.ws = static_cast<uint8_t *>(ws);
   p.stream = (hipStream_t)stream;
-  hipError_t e = launch_route(p);
+  p.events = events;
+  hipEvent_t *ev = (hipEvent_t *)events;
+  hipError_t e = ev ? hipEventRecord(ev[0], p.stream) : hipSuccess;
+  if (e == hipSuccess) e = launch_route(p);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], p.stream);
   if (e == hipSuccess) e = launch_experts(p);
   return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_layer_forward: %s", hipGetErrorString(e));
 }

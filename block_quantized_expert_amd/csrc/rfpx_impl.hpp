@@ -133,7 +133,6 @@ struct RouteTable {
 };
 
 struct WsLayout {
-  size_t counters;  // int32 [1 + n_tiles_down]
   size_t route;     // RouteTable
   size_t scores;    // fp32 [q][E]
   size_t xp;        // u32  [3 fmts][q][nb_d][vx][16]  prepared activations
@@ -142,7 +141,6 @@ struct WsLayout {
   size_t hnc;       // fp32 [slots][q][nb_f]
   size_t part;      // fp32 [slots][q][d]              weighted partial outputs
   size_t total;
-  int n_tiles_down;
   int max_slots;
 };
 
@@ -226,48 +224,69 @@ __device__ __forceinline__ void decode_pairs<RFPX_FP3>(const uint32_t *w, uint32
   p[15] = ((w2 >> 9) & MB) | kOneOne;                                // 73
 }
 
+// Pair p of a block: the codes (and activations) it joins, the factor each
+// activation is stored with, and its share of the accumulator start nc.
+template <int FMT>
+__device__ __forceinline__ void pair_def(int p, int &lo, int &hi, float &slo,
+                                         float &shi) {
+  if (FMT == RFPX_FP2) {
+    lo = 16 * (p >> 3) + (p & 7);
+    hi = lo + 8;
+    slo = shi = 1.f;
+  } else if (FMT == RFPX_FP4) {
+    lo = 8 * (p >> 2) + (p & 3);
+    hi = lo + 4;
+    slo = shi = 1.f;
+  } else if (p < 10) {
+    lo = p < 5 ? p : p + 5;  // 0..4, 10..14
+    hi = lo + 5;
+    slo = 1.f;
+    shi = 2.f;
+  } else {
+    lo = 20 + (p - 10);  // 20..25
+    hi = lo + 6;
+    slo = 4.f;
+    shi = 1.f;
+  }
+}
+
+// nc share of one pair with activations xl, xh (see the header comment):
+// FP2 -(1 + 1.5/8)(xl + xh); FP4 -(1 + 7.5/16)(xl + xh);
+// FP3 -(slo xl + shi xh) - (3.5/8)(xl + xh).
+template <int FMT>
+__device__ __forceinline__ float pair_nc(float xl, float xh, float slo, float shi) {
+  if (FMT == RFPX_FP2) return -1.1875f * (xl + xh);
+  if (FMT == RFPX_FP4) return -1.46875f * (xl + xh);
+  return -(slo * xl + shi * xh) - 0.4375f * (xl + xh);
+}
+
+// bf16 pair word of pair p from bf16 bit patterns of its two activations
+// (the factors 2 and 4 are exact exponent increments).
+template <int FMT>
+__device__ __forceinline__ uint32_t pair_word(uint32_t bl, uint32_t bh, float slo,
+                                              float shi) {
+  if (FMT == RFPX_FP3) {
+    if (slo != 1.f) bl = float_to_bf16_rne(slo * bf16_bits_to_float(bl));
+    if (shi != 1.f) bh = float_to_bf16_rne(shi * bf16_bits_to_float(bh));
+  }
+  return bl | (bh << 16);
+}
+
 // Prepared activations of one block for one virtual column: the 16 bf16
-// pair words matching decode_pairs<FMT> and the accumulator start value nc
-// (see header).  xb[j] are bf16 bit patterns of the block's 32 values.
+// pair words matching decode_pairs<FMT> and the accumulator start nc.  xb[j]
+// are bf16 bit patterns of the block's 32 values.
 template <int FMT>
 __device__ __forceinline__ void prep_pairs(const uint32_t *xb, uint32_t *pw, float *nc) {
-  float X = 0.f;
+  float acc = 0.f;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) X += bf16_bits_to_float(xb[j]);
-  if (FMT == RFPX_FP2) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int a = 0; a < 8; ++a)
-        pw[8 * t + a] = xb[16 * t + a] | (xb[16 * t + a + 8] << 16);
-    *nc = -1.1875f * X;  // -(1 + 1.5/8) X
-  } else if (FMT == RFPX_FP4) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        pw[4 * t + a] = xb[8 * t + a] | (xb[8 * t + a + 4] << 16);
-    *nc = -1.46875f * X;  // -(1 + 7.5/16) X
-  } else {
-    // bf16 *2 and *4 are exact exponent increments (values stay finite)
-    const int loA[10] = {0, 1, 2, 3, 4, 10, 11, 12, 13, 14};
-    float K = 0.f;
-#pragma unroll
-    for (int p = 0; p < 10; ++p) {
-      int lo = loA[p], hi = lo + 5;
-      float xl = bf16_bits_to_float(xb[lo]), xh = bf16_bits_to_float(xb[hi]);
-      pw[p] = xb[lo] | (float_to_bf16_rne(2.f * xh) << 16);
-      K += xl + 2.f * xh;
-    }
-#pragma unroll
-    for (int p = 10; p < 16; ++p) {
-      int lo = 20 + (p - 10), hi = lo + 6;
-      float xl = bf16_bits_to_float(xb[lo]), xh = bf16_bits_to_float(xb[hi]);
-      pw[p] = float_to_bf16_rne(4.f * xl) | (xb[hi] << 16);
-      K += 4.f * xl + xh;
-    }
-    *nc = -K - 0.4375f * X;  // -K - 3.5/8 X
+  for (int p = 0; p < 16; ++p) {
+    int lo, hi;
+    float slo, shi;
+    pair_def<FMT>(p, lo, hi, slo, shi);
+    pw[p] = pair_word<FMT>(xb[lo], xb[hi], slo, shi);
+    acc += pair_nc<FMT>(bf16_bits_to_float(xb[lo]), bf16_bits_to_float(xb[hi]), slo, shi);
   }
+  *nc = acc;
 }
 
 // Block scale as an fp32 multiplier: fp16 bits (FP2/FP3) or E8M0 (FP4).
@@ -333,6 +352,7 @@ struct ForwardPlan {
   int rw_gu, rw_dn;         // rows per workgroup tile
   bool route_only;
   hipStream_t stream;
+  void *const *events;      // optional: 5 hipEvent_t recorded around launches
 };
 hipError_t launch_route(const ForwardPlan &p);
 hipError_t launch_experts(const ForwardPlan &p);

@@ -7,19 +7,23 @@
 // "Lucebox专攻DeepSeek V4…" (m.mzlw.cn), section "MoE 专家并行": 256 routed
 // experts, top-6, plus 1 shared expert per layer.
 //
-// One launch.  Workgroups 0..E-1 compute router scores, one expert per
-// workgroup (the 4 MiB router matrix of d=4096, E=256 is streamed once);
-// workgroups E.. prepare the activations for the expert kernels
-// (bf16 pair words and per-block accumulator starts, see rfpx_impl.hpp).
-// The workgroup that arrives last (device-scope counter) ranks the scores
-// of every column -- k rounds of a wave-wide arg-max, ties to the lower
-// index -- computes the softmax gating weights, and builds the slot table:
-// slot 0 is the shared expert for every column, slots 1.. are the distinct
-// routed experts of all q columns with, for each, the columns that chose it
-// and their weights.  It also clears the counters the down kernel uses.
+// k_route: workgroups 0..E-1 compute the router scores, one expert per
+//   workgroup (the 4 MiB router matrix of d=4096, E=256 is streamed once);
+//   workgroups E.. prepare the activations for the expert kernels (bf16
+//   pair words and per-block accumulator starts, see rfpx_impl.hpp).  No
+//   cross-workgroup synchronization: the next launch reads the scores.
+// route_wg (device function): ranks the scores of every column -- k rounds
+//   of a wave-wide arg-max, ties to the lower index -- computes the softmax
+//   gating weights and builds the slot table in LDS: slot 0 is the shared
+//   expert for every column, slots 1.. are the distinct routed experts of
+//   all q columns in order of first appearance, each with the columns that
+//   chose it and their weights.  The computation is deterministic, so every
+//   workgroup that runs it gets the same table; the gate/up kernel runs it
+//   at its start instead of a separate launch.
+// k_topk: one workgroup running route_wg, for moe_route_topk.
 #include <math.h>
 
-#include "rfpx_impl.hpp"
+#include "rfpx_route.hpp"
 
 namespace rfpx {
 namespace {
@@ -32,20 +36,14 @@ struct RouteArgs {
   const float *wr;
   const void *x;
   float *scores;
-  RouteTable *rt;
-  int *counters;
-  int n_counters;
   int n_router_wg;
   int n_prep_items;
   unsigned prep_fmts;
   uint32_t *xp;
   float *xnc;
-  int32_t *ids_out;
-  float *w_out;
-  int route_only;
 };
 
-__device__ inline float wave_sum(float v) {
+__device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
@@ -59,12 +57,17 @@ __device__ void router_wg(const RouteArgs &a, int e, int tid) {
   constexpr int NPT = 4;
   const int n4 = a.d / 4;
   const float4 *wrow = reinterpret_cast<const float4 *>(a.wr + (size_t)e * a.d);
+  // unconditional loads (clamped index, zeroed after) so that every load is
+  // in flight before the first use
   float4 w[NPT];
 #pragma unroll
   for (int j = 0; j < NPT; ++j) {
-    int i4 = tid + kRouteThreads * j;
-    w[j] = i4 < n4 ? wrow[i4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int i4 = tid + kRouteThreads * j;
+    w[j] = wrow[i4 < n4 ? i4 : n4 - 1];
   }
+#pragma unroll
+  for (int j = 0; j < NPT; ++j)
+    if (tid + kRouteThreads * j >= n4) w[j] = make_float4(0.f, 0.f, 0.f, 0.f);
   float acc[kQMax];
 #pragma unroll
   for (int c = 0; c < kQMax; ++c) {
@@ -73,19 +76,17 @@ __device__ void router_wg(const RouteArgs &a, int e, int tid) {
     float4 xv[NPT];
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      int i4 = tid + kRouteThreads * j;
-      if (i4 >= n4) {
-        xv[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      } else if (a.xtype == RFPX_X_BF16) {
+      const int i4c = min(tid + kRouteThreads * j, n4 - 1);  // w is zero past n4
+      if (a.xtype == RFPX_X_BF16) {
         uint2 b = reinterpret_cast<const uint2 *>(
-            static_cast<const uint16_t *>(a.x) + (size_t)c * a.d)[i4];
+            static_cast<const uint16_t *>(a.x) + (size_t)c * a.d)[i4c];
         xv[j] = make_float4(__uint_as_float(b.x << 16),
                             __uint_as_float(b.x & 0xFFFF0000u),
                             __uint_as_float(b.y << 16),
                             __uint_as_float(b.y & 0xFFFF0000u));
       } else {
         xv[j] = reinterpret_cast<const float4 *>(
-            static_cast<const float *>(a.x) + (size_t)c * a.d)[i4];
+            static_cast<const float *>(a.x) + (size_t)c * a.d)[i4c];
       }
     }
 #pragma unroll
@@ -144,157 +145,48 @@ __device__ void prep_item(const RouteArgs &a, int c, int b) {
   a.xnc[item] = nc_hi + nc_lo;
 }
 
-// Rank the E scores of one column (one wave): k rounds of arg-max over
-// (score descending, index ascending).
-__device__ void topk_wave(const RouteArgs &a, int c, int lane, int32_t *ids,
-                          float *vals) {
-  constexpr int PER = kEMax / 64;
-  float sv[PER];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    int e = lane + 64 * i;
-    sv[i] = e < a.E ? a.scores[(size_t)c * a.E + e] : -INFINITY;
-  }
-  for (int r = 0; r < a.k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      int e = lane + 64 * i;
-      bool ok = e < a.E && !((taken >> i) & 1u);
-      if (ok && (sv[i] > bv || (sv[i] == bv && e < bi))) {
-        bv = sv[i];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      float ov = __shfl_xor(bv, off, 64);
-      int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    ids[r] = bi;
-    vals[r] = bv;
-  }
-}
-
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int bid = blockIdx.x;
   if (bid < a.n_router_wg) {
     router_wg(a, bid, tid);
-  } else {
-    int item = (bid - a.n_router_wg) * kRouteThreads + tid;
-    if (item < a.n_prep_items) {
-      // items run over (format present, column, block)
-      int per_fmt = a.q * a.nb_d;
-      int nth = item / per_fmt, rem = item % per_fmt;
-      int c = rem / a.nb_d, b = rem % a.nb_d;
-      int fmt = 0;
-      for (int f = RFPX_FP2, seen = 0; f <= RFPX_FP4; ++f)
-        if ((a.prep_fmts >> f) & 1u) {
-          if (seen == nth) fmt = f;
-          ++seen;
-        }
-      if (fmt == RFPX_FP2) prep_item<RFPX_FP2>(a, c, b);
-      else if (fmt == RFPX_FP3) prep_item<RFPX_FP3>(a, c, b);
-      else if (fmt == RFPX_FP4) prep_item<RFPX_FP4>(a, c, b);
-    }
+    return;
   }
+  int item = (bid - a.n_router_wg) * kRouteThreads + tid;
+  if (item >= a.n_prep_items) return;
+  // items run over (format present, column, block)
+  int per_fmt = a.q * a.nb_d;
+  int nth = item / per_fmt, rem = item % per_fmt;
+  int c = rem / a.nb_d, b = rem % a.nb_d;
+  int fmt = 0;
+  for (int f = RFPX_FP2, seen = 0; f <= RFPX_FP4; ++f)
+    if ((a.prep_fmts >> f) & 1u) {
+      if (seen == nth) fmt = f;
+      ++seen;
+    }
+  if (fmt == RFPX_FP2) prep_item<RFPX_FP2>(a, c, b);
+  else if (fmt == RFPX_FP3) prep_item<RFPX_FP3>(a, c, b);
+  else if (fmt == RFPX_FP4) prep_item<RFPX_FP4>(a, c, b);
+}
 
-  // ---- last workgroup to arrive ranks, gates and batches
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    int prev = __hip_atomic_fetch_add(&a.counters[0], 1, __ATOMIC_ACQ_REL,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == (int)gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+struct TopkArgs {
+  RouteParams rp;
+  RouteTable *rt;
+  int32_t *ids_out;
+  float *w_out;
+};
 
-  __shared__ int32_t s_ids[kQMax][kKMax];
-  __shared__ float s_gw[kQMax][kKMax];
-  for (int c = wave; c < a.q; c += kRouteThreads / 64) {
-    int32_t ids[kKMax];
-    float vals[kKMax];
-    topk_wave(a, c, lane, ids, vals);
-    if (lane == 0) {
-      float z = 0.f;
-      for (int j = 0; j < a.k; ++j) z += expf(vals[j] - vals[0]);
-      for (int j = 0; j < a.k; ++j) {
-        float w = expf(vals[j] - vals[0]) / z * a.routed_scale;
-        s_ids[c][j] = ids[j];
-        s_gw[c][j] = w;
-        a.rt->ids[c][j] = ids[j];
-        a.rt->gw[c][j] = w;
-        if (a.ids_out) a.ids_out[c * a.k + j] = ids[j];
-        if (a.w_out) a.w_out[c * a.k + j] = w;
-      }
-    }
+__global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
+  __shared__ RouteLds s;
+  route_wg(a.rp, &s);
+  const int tid = threadIdx.x;
+  const int q = a.rp.q, k = a.rp.k;
+  for (int i = tid; i < q * k; i += blockDim.x) {
+    const int c = i / k, j = i % k;
+    a.ids_out[i] = s.ids[c][j];
+    a.w_out[i] = s.gw[c][j];
   }
-  __syncthreads();
-  if (tid == 0) a.counters[0] = 0;  // every other workgroup has arrived
-  if (a.route_only) return;
-  for (int i = 1 + tid; i < a.n_counters; i += kRouteThreads) a.counters[i] = 0;
-
-  if (wave == 0) {
-    // lane i < n holds entry (column i / k, rank i % k)
-    const int n = a.q * a.k;
-    int e = -1, c = 0;
-    float w = 0.f;
-    if (lane < n) {
-      c = lane / a.k;
-      e = s_ids[c][lane % a.k];
-      w = s_gw[c][lane % a.k];
-    }
-    int first = lane;
-    for (int j = 0; j < n; ++j) {
-      int ej = __shfl(e, j, 64);
-      if (lane < n && ej == e && j < first) first = j;
-    }
-    bool is_first = lane < n && first == lane;
-    uint64_t firsts = __ballot(is_first);
-    int slot = 1 + __popcll(firsts & ((1ull << lane) - 1ull));
-    slot = __shfl(slot, first, 64);
-    int pos = 0, cnt = 0;
-    uint32_t mask = 0;
-    for (int j = 0; j < n; ++j) {
-      int sj = __shfl(slot, j, 64), cj = __shfl(c, j, 64);
-      if (sj == slot) {
-        ++cnt;
-        if (j < lane) ++pos;
-        mask |= 1u << cj;
-      }
-    }
-    RouteTable *rt = a.rt;
-    if (lane < n) {
-      rt->cols[slot][pos] = c;
-      rt->w[slot][pos] = w;
-      if (is_first) {
-        rt->expert[slot] = e;
-        rt->ncols[slot] = cnt;
-        rt->mask[slot] = mask;
-      }
-    }
-    if (lane == 0) {
-      rt->nslots = 1 + __popcll(firsts);
-      rt->expert[0] = a.E;
-      rt->ncols[0] = a.q;
-      rt->mask[0] = (1u << a.q) - 1u;
-    }
-    if (lane < a.q) {
-      rt->cols[0][lane] = lane;
-      rt->w[0][lane] = 1.0f;
-    }
-  }
+  publish_route(s, q, -1, true, a.rt);  // the whole table
 }
 
 }  // namespace
@@ -312,20 +204,22 @@ hipError_t launch_route(const ForwardPlan &p) {
   a.wr = p.router_w;
   a.x = p.x;
   a.scores = reinterpret_cast<float *>(p.ws + p.wl.scores);
-  a.rt = reinterpret_cast<RouteTable *>(p.ws + p.wl.route);
-  a.counters = reinterpret_cast<int *>(p.ws + p.wl.counters);
-  a.n_counters = 1 + p.wl.n_tiles_down;
   a.n_router_wg = p.E;
   int nf = __builtin_popcount(p.prep_fmts);
   a.n_prep_items = p.route_only ? 0 : nf * p.q * (p.d / 32);
   a.prep_fmts = p.prep_fmts;
   a.xp = reinterpret_cast<uint32_t *>(p.ws + p.wl.xp);
   a.xnc = reinterpret_cast<float *>(p.ws + p.wl.xnc);
-  a.ids_out = p.ids_out;
-  a.w_out = p.w_out;
-  a.route_only = p.route_only ? 1 : 0;
   int n_prep_wg = (a.n_prep_items + kRouteThreads - 1) / kRouteThreads;
   k_route<<<a.n_router_wg + n_prep_wg, kRouteThreads, 0, p.stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.route_only) return e;
+  TopkArgs t{};
+  t.rp = route_params(p);
+  t.rt = reinterpret_cast<RouteTable *>(p.ws + p.wl.route);
+  t.ids_out = p.ids_out;
+  t.w_out = p.w_out;
+  k_topk<<<1, 512, 0, p.stream>>>(t);
   return hipGetLastError();
 }
 

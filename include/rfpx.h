@@ -162,9 +162,8 @@ rfpx_status moe_image_unpack(const moe_layer *L, int expert, int matrix,
 
 /* Workspace for moe_route_topk / moe_layer_forward with q columns
  * (prefill = 0), or for moe_prefill_forward with T tokens (prefill = 1);
- * 0 if the shape is unsupported.  The workspace must be 256-byte aligned and
- * zero-filled before its first use; every call leaves its counters at zero
- * again, so it is then reusable without clearing. */
+ * 0 if the shape is unsupported.  The workspace must be 256-byte aligned;
+ * its contents need no initialization and are scratch between calls. */
 size_t moe_workspace_bytes(const moe_layer *L, int q_or_T, int prefill);
 
 /* Router scores, top-k and gating for q columns of x_dev ([q][d] fp32 or
@@ -180,6 +179,17 @@ rfpx_status moe_route_topk(const moe_layer *L, const void *x_dev, int xtype,
 rfpx_status moe_layer_forward(const moe_layer *L, const void *x_dev, int xtype,
                               int q, float *y_dev, void *ws_dev,
                               size_t ws_bytes, void *stream);
+
+/* moe_layer_forward that also records caller-created hipEvent_t handles on
+ * `stream`: events[0] before the router kernel, events[1] after it,
+ * events[2] after the gate/up kernel, events[3] after the down kernel,
+ * events[4] after the combine kernel.  For measuring each kernel of a step
+ * inside a timed loop; events may be NULL (then it is moe_layer_forward).
+ * The events must belong to the current device. */
+rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x_dev,
+                                    int xtype, int q, float *y_dev,
+                                    void *ws_dev, size_t ws_bytes,
+                                    void *stream, void *const *events);
 
 /* One prefill chunk of T tokens (x_dev [T][d] bf16 or fp32): tokens are
  * grouped by expert and each expert runs as a dense grouped product on the
