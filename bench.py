@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer decode tokens/s and packed-weight HBM GB/s (% of peak) at q=1,4,5"
 HBM_PEAK_GBS = 8000.0
+HIP_EVENT_RELEASE_TO_DEVICE = 0x40000000  # hipEventReleaseToDevice
 
 
 class HipEvents:
@@ -52,7 +53,7 @@ class HipEvents:
         if path is None:
             raise RuntimeError("HIP runtime not loaded")
         self.lib = C.CDLL(path)
-        self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
         self.lib.hipEventDestroy.argtypes = [C.c_void_p]
 
@@ -60,8 +61,10 @@ class HipEvents:
         arr = (C.c_void_p * n)()
         for i in range(n):
             h = C.c_void_p()
-            if self.lib.hipEventCreate(C.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            # device-scope release: a timing event then costs no write-back
+            # of the caches to system scope between the kernels it separates
+            if self.lib.hipEventCreateWithFlags(C.byref(h), HIP_EVENT_RELEASE_TO_DEVICE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             arr[i] = h
         return arr
 
@@ -89,6 +92,40 @@ def expert_bytes(lay, e):
     return tot, gu
 
 
+KERNEL_SOURCES = ("expert.hip", "rfpx_impl.hpp", "rfpx_route.hpp", "abi.hip")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the sources that define the decode kernels and their launch."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_quantized_expert_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary of `kernel` on
+    `workload` (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +138,9 @@ def main() -> int:
                     help="activation batches per layer instance")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall time budget of the CPU oracle sample (0: skip)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one plain fp32 copy kernel (torch.neg) of this many MiB "
+                         "before the timed region, to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path has no multi-GPU mode "
@@ -163,6 +203,17 @@ def main() -> int:
             bqe.moe_layer_forward(L, x, y=y, ws=ws)
         else:
             bqe.moe_layer_forward_timed(L, x, y, ws, events)
+
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 18)
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(f"# calibration copy: {4 * n} bytes read, {4 * n} bytes written",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     for li, vi in warm:
         step(li, vi)
@@ -262,7 +313,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gu_gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("k_gateup", cfg.name),
             "bytes_per_launch": gu_bytes,
         },
         "cpu_baseline": cpu,

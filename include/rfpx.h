@@ -145,8 +145,8 @@ rfpx_status moe_image_build(int d, int f, int n_experts, const int *fmts_host,
                             uint8_t *image_dev, size_t cap, void *stream);
 
 typedef struct {
-  int d;              /* model width, a power of two from 256 to 16384 */
-  int f;              /* expert width, a power of two from 64 to 8192 */
+  int d;              /* model width, a power of two from 256 to 4096 */
+  int f;              /* expert width, a power of two from 64 to 4096 */
   int n_experts;      /* routed experts E, 1..RFPX_E_MAX */
   int top_k;          /* k, 1..min(E, RFPX_K_MAX) */
   float routed_scale; /* multiplies the k gating weights (1.0) */
