@@ -17,8 +17,9 @@ weight is re-read from the 256 MB last-level cache within a rotation.
 Timing: W warm-up steps, then K steps between two synchronizations, timed
 with events on the stream the kernels run on.  A second pass of K steps
 records a hipEvent between the three kernels of every step
-(moe_layer_forward_timed) to time the dominant kernel (gate/up) for the
-roofline entry.  The CPU oracle is timed on a bounded sample on the host.
+(moe_layer_forward_timed) to time the dominant kernel (the gate/up kernel)
+for the roofline entry.  The CPU oracle is timed on a bounded sample
+on the host.
 
 Prints one JSON line.
 """
@@ -80,6 +81,7 @@ class HipEvents:
 
 
 def expert_bytes(lay, e):
+    """(all packed bytes, gate + up bytes) of expert e."""
     import synth
     tot = 0
     gu = 0
@@ -236,7 +238,7 @@ def main() -> int:
 
     # ---- timed pass: kernels of each step
     he = HipEvents()
-    evs = [he.create(5) for _ in order]
+    evs = [he.create(4) for _ in order]
     torch.cuda.synchronize()
     t0.record()
     for (li, vi), ev in zip(order, evs):
@@ -247,7 +249,6 @@ def main() -> int:
     k_route = [he.elapsed_ms(ev[0], ev[1]) for ev in evs]
     k_gu = [he.elapsed_ms(ev[1], ev[2]) for ev in evs]
     k_dn = [he.elapsed_ms(ev[2], ev[3]) for ev in evs]
-    k_cb = [he.elapsed_ms(ev[3], ev[4]) for ev in evs]
     for ev in evs:
         he.destroy(ev)
     gu_us = 1e3 * float(np.mean(k_gu))
@@ -300,15 +301,14 @@ def main() -> int:
             "router_bytes_per_step": cfg.E * cfg.d * 4,
         },
         "kernels_us": {
-            "route_topk": 1e3 * float(np.mean(k_route)),
-            "gate_up": gu_us,
-            "down": 1e3 * float(np.mean(k_dn)),
-            "combine": 1e3 * float(np.mean(k_cb)),
+            "k_route (router scores + prepared activations)": 1e3 * float(np.mean(k_route)),
+            "k_gateup (routing + gate/up of the shared and routed experts)": gu_us,
+            "k_down (down of all slots + combine)": 1e3 * float(np.mean(k_dn)),
             "step_with_events": total_ev_ms * 1e3 / args.steps,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gateup (gate/up dequant-GEMV + SiLU, routed and shared)",
+            "kernel": "k_gateup (routing + gate/up dequant-GEMV + SiLU, shared and routed)",
             "achieved": gu_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -290,9 +290,11 @@ def moe_layer_forward(layer: MoeLayer, x, y=None, ws=None, stream=None):
 
 
 def moe_layer_forward_timed(layer: MoeLayer, x, y, ws, events, stream=None):
-    """events: a ctypes array of 5 hipEvent_t handles (created by the
-    caller on this device), recorded around the four kernels."""
+    """events: a ctypes array of 4 hipEvent_t handles (created by the
+    caller on this device), recorded around the three kernels."""
     _need_cuda(x)
+    if events is not None and len(events) != 4:
+        raise ValueError("moe_layer_forward_timed takes 4 events")
     _check("moe_layer_forward_timed", lib().moe_layer_forward_timed(
         layer.ref, _ptr(x), _xtype(x), x.shape[0], _ptr(y), _ptr(ws), ws.numel(),
         _stream(stream), C.cast(events, C.c_void_p) if events is not None else None))

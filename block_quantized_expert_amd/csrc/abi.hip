@@ -57,29 +57,30 @@ bool pow2_in(int v, int lo, int hi) {
   return v >= lo && v <= hi && (v & (v - 1)) == 0;
 }
 
-// Rows per workgroup tile.  A unit is r rows (rpi rows per wave step) of one
-// column part (tpl parts per row); the waves of a workgroup loop over the
-// tile's units.  Gate/up tiles hold whole 32-row blocks of h (the down
-// matrix's blocks); down tiles aim at one unit per wave.
-bool pick_tile_gateup(const Geo *geo, unsigned fmts, int r, int rows, int *rw) {
+// Rows per workgroup tile.  A unit is R rows (rpi rows per wave step) of one
+// column part; R depends on the format and the pass width (unit_rows_for).
+// Gate/up tiles hold whole 32-row blocks of h (the down matrix's blocks).
+bool pick_tile_gateup(const Geo *geo, unsigned fmts, int g, int rows, int *rw) {
   int t = 32;
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
-    if ((fmts >> f) & 1u) t = t > geo[f].rpi * r ? t : geo[f].rpi * r;
+    if ((fmts >> f) & 1u) {
+      const int unit = geo[f].rpi * unit_rows_for(f, g);
+      t = t > unit ? t : unit;
+    }
   if (t > rows || rows % t) return false;
   *rw = t;
   return true;
 }
 
-bool pick_tile_down(const Geo *geo, unsigned fmts, int r, int waves, int rows, int *rw) {
-  int lo = 1, hi = rows;
-  for (int f = RFPX_FP2; f <= RFPX_FP4; ++f) {
-    if (!((fmts >> f) & 1u)) continue;
-    const int unit = geo[f].rpi * r;
-    const int want = unit * waves / geo[f].tpl;
-    lo = lo > unit ? lo : unit;
-    hi = hi < want ? hi : want;
-  }
-  const int t = hi > lo ? hi : lo;
+// Down tiles: about 512 workgroups over the d rows (two per compute unit),
+// and at least one unit of every present format.
+bool pick_tile_down(const Geo *geo, unsigned fmts, int g, int rows, int *rw) {
+  int t = rows / 512 > 1 ? rows / 512 : 1;
+  for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
+    if ((fmts >> f) & 1u) {
+      const int unit = geo[f].rpi * unit_rows_for(f, g);
+      t = t > unit ? t : unit;
+    }
   if (t > rows || rows % t) return false;
   *rw = t;
   return true;
@@ -123,11 +124,11 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   p->router_w = L->router_w;
   p->image = L->image;
   for (int e = 0; e <= L->n_experts; ++e) {
-    p->prep_fmts |= 1u << L->fmts[3 * e];
+    p->gu_fmts |= 1u << L->fmts[3 * e];
     p->down_fmts |= 1u << L->fmts[3 * e + 2];
   }
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f) {
-    if ((p->prep_fmts >> f) & 1u) {
+    if ((p->gu_fmts >> f) & 1u) {
       if (!make_geo(f, L->d, &p->geo_gu[f]) || p->geo_gu[f].tpl > 2)
         return fail(RFPX_E_SHAPE, "d=%d does not tile for gate/up format %d", L->d, f);
     }
@@ -137,22 +138,25 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
     }
   }
   p->g = q == 1 ? 1 : 2;
-  p->r = 4;     // rows per unit: must match the kernels' R template
-  p->wmax = 8;  // waves per workgroup
-  if (!pick_tile_gateup(p->geo_gu, p->prep_fmts, p->r, L->f, &p->rw_gu))
+  p->wmax = 8;  // waves per workgroup (a multiple of the column parts, 1 or 2)
+  if (!pick_tile_gateup(p->geo_gu, p->gu_fmts, p->g, L->f, &p->rw_gu))
     return fail(RFPX_E_SHAPE, "f=%d: no gate/up tile for this format mix", L->f);
-  if (!pick_tile_down(p->geo_dn, p->down_fmts, p->r, p->wmax, L->d, &p->rw_dn))
+  if (!pick_tile_down(p->geo_dn, p->down_fmts, p->g, L->d, &p->rw_dn))
     return fail(RFPX_E_SHAPE, "d=%d: no down tile for this format mix", L->d);
+  if ((size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024)
+    return fail(RFPX_E_SHAPE, "f=%d, q=%d: down tile of %d rows needs too much LDS", L->f, q,
+                p->rw_dn);
 
   WsLayout &w = p->wl;
-  const int vx = xtype == RFPX_X_BF16 ? 1 : 2;
-  const int nb_d = L->d / 32, nb_f = L->f / 32;
+  const int nb_f = L->f / 32;
   w.max_slots = 1 + (q * L->top_k < L->n_experts ? q * L->top_k : L->n_experts);
   size_t off = 0;
   w.route = off;
   off = align_up(off + sizeof(RouteTable), 256);
   w.scores = off;
   off = align_up(off + (size_t)q * L->n_experts * 4, 256);
+  const int vx = xtype == RFPX_X_BF16 ? 1 : 2;
+  const int nb_d = L->d / 32;
   w.xp = off;
   off = align_up(off + (size_t)3 * q * nb_d * vx * 16 * 4, 256);
   w.xnc = off;
@@ -161,8 +165,6 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   off = align_up(off + (size_t)w.max_slots * q * nb_f * 32 * 4, 256);
   w.hnc = off;
   off = align_up(off + (size_t)w.max_slots * q * nb_f * 4, 256);
-  w.part = off;
-  off = align_up(off + (size_t)w.max_slots * q * L->d * 4, 256);
   w.total = off;
   return RFPX_OK;
 }

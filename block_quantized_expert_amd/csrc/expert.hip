@@ -1,34 +1,41 @@
-// expert.hip -- expert-grouped dequantize-and-GEMV for the routed and the
-// shared experts, decode path.
+// expert.hip -- the decode step of one routed-MoE layer: router scores, the
+// shared and routed experts' dequantize-and-GEMV products with SiLU gating,
+// and the weighted combine.
 //
 // Page "APU 实现 token 自由…" (ainomam.com), section "Lucebox 的优化三板斧":
 // in the q-column verify path each packed weight is decoded once and applied
 // to every verify column.  Page "Lucebox专攻DeepSeek V4…" (m.mzlw.cn),
-// section "常见疑问" (FAQ): decode is bound by memory bandwidth.
+// sections "MoE 专家并行" (256 routed experts, top-6, one shared expert) and
+// "新手常见疑问" (decode is bound by memory bandwidth).  Page "DeepSeek V4
+// Flash 在 128GB 锐龙 AI MAX+ 上跑到 32 tok/s" (taozi.news), section
+// "ROCmFPX": gate/up in FP2, down in FP3, the shared expert in FP4.
 //
-// Three launches after the router (route.hip):
-//   k_gateup  grid (f / RW, slots).  Workgroups of routed slots first run
-//             the routing step in LDS (rfpx_route.hpp; deterministic, so all
-//             agree); workgroup (0, s) publishes slot s for the launches that
-//             follow.  Workgroups of slot 0 (the shared expert) need no
-//             routing and start streaming at once.  A workgroup owns RW
-//             consecutive rows of the gate and up matrices of its slot's
-//             expert; each wave owns R rows of both, issues every code and
-//             scale load for them up front (buffer loads: scalar descriptor,
-//             scalar row offset, 32-bit lane offset), decodes each block in
-//             registers once and applies it to all of the slot's columns
-//             (v_dot2c_f32_bf16 on the prepared activations), reduces each
-//             row across its lanes and forms h = silu(g) * u.  The workgroup
-//             then prepares h for the down matrix (bf16 hi + lo pair words,
-//             one thread per pair word).
-//   k_down    grid (d / RW, slots): the same over the down matrix; each row
-//             result times the column's gating weight is stored as a
-//             partial.
-//   k_combine y[c][i] = sum over slots (in slot order) of the partials:
-//             deterministic, no atomics, no device-scope fences.
+// Launches per step (after k_route, route.hip: router scores and prepared
+// activations):
+//   k_gateup  grid (f / RW_GU, slots).  Slot 0 is the shared expert (every
+//             column, weight 1): its workgroups need no routing and start
+//             streaming at once.  Workgroups of routed slots first run the
+//             routing step in LDS (sorted top-k, gating, slot table;
+//             deterministic, so all workgroups agree; rfpx_route.hpp) and
+//             workgroup (0, s) publishes slot s; then a gate/up tile of the
+//             slot's expert.
+//   k_down    grid d / RW_DN.  A workgroup owns RW_DN rows of y for every
+//             column and runs the down rows of every slot into them, each
+//             row result times the column's gating weight: the combine is
+//             its epilogue, and no partial output leaves the workgroup.
+//
+// A gate/up tile is RW_GU rows of the gate and up matrices (whole 32-row
+// blocks of h).  It is cut into units of R rows x one part of 64 chunks per
+// row; each wave loads the prepared activations of its chunk once per pass,
+// issues every code and scale load of a unit up front (buffer loads: scalar
+// descriptor, scalar row offset, 32-bit lane offset), decodes each block in
+// registers once for all columns of the pass (v_dot2 on the prepared
+// pairs), reduces each row across its lanes with DPP and writes part sums to
+// LDS.  Then h = silu(g) * u, and the workgroup prepares h for the down
+// matrix (bf16 hi + lo pair words) so k_down only loads it.
 // Lane geometry (Geo): with a row of >= 64 chunks a wave covers one row per
-// step and lane l reads chunks l and l+64 (fully coalesced 1 KiB requests);
-// shorter rows give each wave 64/cpl rows per step.
+// step and lane l reads chunk l (+ 64 for the second part; fully coalesced
+// 1 KiB requests); shorter rows give each wave 64/cpl rows per step.
 #include "rfpx_route.hpp"
 
 namespace rfpx {
@@ -38,11 +45,10 @@ struct ExpArgs {
   const uint8_t *image;
   RouteTable *rt;
   RouteParams rp;
-  const uint32_t *xp;
-  const float *xnc;
-  uint32_t *hp;
-  float *hnc;
-  float *part;
+  const uint32_t *xp;   // prepared activations [fmt][q][nb_d][vx][16]
+  const float *xnc;     // [fmt][q][nb_d]
+  uint32_t *hp;         // prepared h [slot][q][nb_f][2][16]
+  float *hnc;           // [slot][q][nb_f]
   float *y;
   int d, f, q, nb_d, nb_f;
   int rw_gu, rw_dn;
@@ -50,17 +56,17 @@ struct ExpArgs {
 };
 
 // The columns of one slot: expert and count in scalar registers; the column
-// list and weights stay in LDS or the workspace table and are read when a
-// pass needs them (indexing a register array by a loop counter would put it
-// in scratch memory).
+// list and weights stay in LDS and are read when a pass needs them (indexing
+// a register array by a loop counter would put it in scratch memory).  Both
+// accessors take a wave-uniform index and return the first lane's value.
 struct SlotCols {
   int expert, ncols;
   const int *cols;   // [ncols] global column index of each compact column
   const float *w;    // [ncols] gating weight
-  // i must be wave-uniform (the result is taken from the first lane)
   __device__ int col(int i) const { return uniform(cols[i]); }
-  // i may differ between lanes
-  __device__ float weight(int i) const { return w[i]; }
+  __device__ float weight(int i) const {
+    return __int_as_float(uniform(__float_as_int(w[i])));
+  }
 };
 
 template <int FMT>
@@ -107,24 +113,15 @@ struct MatPtr {
   __amdgpu_buffer_rsrc_t scales;
 };
 
-// Per-lane partial dot products of R rows of NM matrices with G columns for
-// one "unit": rows row_u + rpi*i (i < R) of one column part, the lane's own
-// chunk at byte offsets coff (codes) and soff (scales) within a row.  Rows
-// are read through the matrix planes' buffer resources at scalar offset
-// row * pitch (row_u is wave-uniform).  All code and scale loads are issued
-// first; then rows are decoded one at a time (scheduling fences keep the
-// decode of one row from being hoisted over the next, which would multiply
-// register pressure).
-template <int FMT, int G, int VX, int NM, int R>
-__device__ __forceinline__ void unit_rows(const MatPtr (&mats)[NM], uint32_t cpitch,
-                                          uint32_t spitch, int row_u, int rpi,
-                                          uint32_t coff, uint32_t soff,
-                                          const uint32_t (&xr)[G][Fmt<FMT>::CB][VX][16],
-                                          const float (&ncr)[G][Fmt<FMT>::CB],
-                                          float (&tot)[R][NM][G]) {
-  using F = Fmt<FMT>;
-  uint32_t cw[R][NM][F::CW];
-  uint32_t sw[R][NM];
+// Code and scale loads of one unit: rows row_u + rpi*i (i < R) of NM
+// matrices, the lane's own chunk at byte offsets coff (codes) and soff
+// (scales) within a row; rows are addressed through the planes' buffer
+// resources at scalar offset row * pitch (row_u is wave-uniform).
+template <int FMT, int NM, int R>
+__device__ __forceinline__ void unit_load(const MatPtr (&mats)[NM], uint32_t cpitch,
+                                          uint32_t spitch, int row_u, int rpi, uint32_t coff,
+                                          uint32_t soff, uint32_t (&cw)[R][NM][Fmt<FMT>::CW],
+                                          uint32_t (&sw)[R][NM]) {
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const uint32_t row = (uint32_t)(row_u + rpi * i);
@@ -134,6 +131,20 @@ __device__ __forceinline__ void unit_rows(const MatPtr (&mats)[NM], uint32_t cpi
       sw[i][m] = load_scale<FMT>(mats[m].scales, soff, row * spitch);
     }
   }
+}
+
+// Per-lane partial dot products of the unit's rows with G columns of
+// prepared activations: each row's blocks are decoded once and applied to
+// every column.  Rows are decoded one at a time (scheduling fences keep the
+// decode of one row from being hoisted over the next, which would multiply
+// register pressure).
+template <int FMT, int G, int VX, int NM, int R>
+__device__ __forceinline__ void unit_compute(const uint32_t (&cw)[R][NM][Fmt<FMT>::CW],
+                                             const uint32_t (&sw)[R][NM],
+                                             const uint32_t (&xr)[G][Fmt<FMT>::CB][VX][16],
+                                             const float (&ncr)[G][Fmt<FMT>::CB],
+                                             uint32_t one, float (&tot)[R][NM][G]) {
+  using F = Fmt<FMT>;
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
@@ -145,7 +156,7 @@ __device__ __forceinline__ void unit_rows(const MatPtr (&mats)[NM], uint32_t cpi
 #pragma unroll
       for (int j = 0; j < F::CB; ++j) {
         uint32_t pr[16];
-        decode_pairs<FMT>(&cw[i][m][j * F::BW], pr);
+        decode_pairs<FMT>(&cw[i][m][j * F::BW], pr, one);
         const float s = block_scale<FMT>(block_scale_bits<FMT>(sw[i][m], j));
 #pragma unroll
         for (int g = 0; g < G; ++g) {
@@ -161,24 +172,54 @@ __device__ __forceinline__ void unit_rows(const MatPtr (&mats)[NM], uint32_t cpi
   }
 }
 
-// Prepared activations (or prepared h) of the blocks of chunk `ch` for G
-// columns: block b of column c sits at ((c * nb) + b) * VX * 16 words, its
-// accumulator start at c * nb + b.
+// Prepared activations of the blocks of the lane's chunk `ch` for columns
+// colidx[0..G) (format FMT): block b of column c sits at ((c * nb) + b) *
+// VX * 16 words, its accumulator start at c * nb + b.
 template <int FMT, int G, int VX>
-__device__ __forceinline__ void load_prepared(const uint32_t *__restrict__ pw,
-                                              const float *__restrict__ pnc, int nb,
-                                              const int *colidx, int ch,
-                                              uint32_t (&xr)[G][Fmt<FMT>::CB][VX][16],
-                                              float (&ncr)[G][Fmt<FMT>::CB]) {
+__device__ __forceinline__ void load_prepared_x(const ExpArgs &a, const int (&colidx)[G],
+                                                int ch, uint32_t (&xr)[G][Fmt<FMT>::CB][VX][16],
+                                                float (&ncr)[G][Fmt<FMT>::CB]) {
+  using F = Fmt<FMT>;
+  const uint32_t *pw = a.xp + (size_t)(FMT - RFPX_FP2) * a.q * a.nb_d * VX * 16;
+  const float *pnc = a.xnc + (size_t)(FMT - RFPX_FP2) * a.q * a.nb_d;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int j = 0; j < F::CB; ++j) {
+      const size_t item = (size_t)colidx[g] * a.nb_d + ch * F::CB + j;
+      const uint4 *src = reinterpret_cast<const uint4 *>(pw + item * VX * 16);
+#pragma unroll
+      for (int v = 0; v < VX; ++v)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 q4 = src[v * 4 + u];
+          xr[g][j][v][4 * u + 0] = q4.x;
+          xr[g][j][v][4 * u + 1] = q4.y;
+          xr[g][j][v][4 * u + 2] = q4.z;
+          xr[g][j][v][4 * u + 3] = q4.w;
+        }
+      ncr[g][j] = pnc[item];
+    }
+  }
+}
+
+// Prepared h of the blocks of chunk `ch` for G compact columns c0.. of a
+// slot: block b of column c sits at ((c * nb) + b) * 32 words (16 hi, 16
+// lo), its accumulator start at c * nb + b.
+template <int FMT, int G>
+__device__ __forceinline__ void load_prepared_h(const uint32_t *__restrict__ pw,
+                                                const float *__restrict__ pnc, int nb, int c0,
+                                                int ch, uint32_t (&xr)[G][Fmt<FMT>::CB][2][16],
+                                                float (&ncr)[G][Fmt<FMT>::CB]) {
   using F = Fmt<FMT>;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
 #pragma unroll
     for (int j = 0; j < F::CB; ++j) {
-      const size_t item = (size_t)colidx[g] * nb + ch * F::CB + j;
-      const uint4 *src = reinterpret_cast<const uint4 *>(pw + item * VX * 16);
+      const size_t item = (size_t)(c0 + g) * nb + ch * F::CB + j;
+      const uint4 *src = reinterpret_cast<const uint4 *>(pw + item * 32);
 #pragma unroll
-      for (int v = 0; v < VX; ++v)
+      for (int v = 0; v < 2; ++v)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const uint4 q4 = src[v * 4 + u];
@@ -226,9 +267,9 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
   return v;
 }
 
-// Where a wave's unit lies: unit u covers rows [rg0, rg0 + R*rpi) of the
-// tile (rows rg0 + rg + rpi*i for the lane's row group rg) and column part
-// p (chunks 64p .. 64p+63 of each row when a row has 128 chunks).
+// Where a unit lies: unit u covers rows [rloc_u, rloc_u + R*rpi) of the tile
+// (rows rloc_u + rg + rpi*i for the lane's row group rg) and column part
+// u % parts (chunks 64p .. 64p+63 of each row when a row has 128 chunks).
 struct UnitPos {
   int rloc_u;   // first row of the unit within the tile (wave-uniform)
   int part;     // column part
@@ -243,76 +284,96 @@ __device__ __forceinline__ UnitPos unit_pos(int u, int parts, int r, int rpi) {
 
 // ------------------------------------------------------------ gate / up
 
-// One unit of GP columns (c0 .. c0+GP-1 of the slot): per-lane partials of
-// gate and up rows, reduced across the lanes, written as part sums to LDS.
+// One pass of GP columns (c0 .. c0+GP-1 of the slot) over the wave's units
+// u = wave, wave + waves, ... (all in part wave % P, since waves is a
+// multiple of P): the first unit's weight loads go out, then the prepared
+// activations of the wave's chunk are loaded (once for all its units), then
+// each unit is decoded, reduced across lanes, and written as part sums to
+// LDS.
 template <int FMT, int GP, int VX, int R>
-__device__ __forceinline__ void gateup_unit(const ExpArgs &a, const SlotCols &sc, int c0,
-                                            const Geo &geo, const UnitPos &up, int tile,
-                                            const MatPtr (&mats)[2], uint32_t cpitch,
-                                            uint32_t spitch, float *gup /* [2][P][kQMax][rw] */) {
+__device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc, int c0,
+                                            const Geo &geo, int units, int wave, int waves,
+                                            int tile, const MatPtr (&mats)[2], uint32_t cpitch,
+                                            uint32_t spitch, float *gup /* [2][P][q][rw] */) {
   using F = Fmt<FMT>;
   const int lane = threadIdx.x & 63;
   const int rg = lane / geo.lpr, li = lane % geo.lpr;
-  const int ch = li + geo.lpr * up.part;
-  const uint32_t *xpf = a.xp + (size_t)(FMT - RFPX_FP2) * a.q * a.nb_d * VX * 16;
-  const float *xncf = a.xnc + (size_t)(FMT - RFPX_FP2) * a.q * a.nb_d;
+  const int P = geo.tpl, rw = a.rw_gu, q = a.q;
   int colidx[GP];
 #pragma unroll
   for (int g = 0; g < GP; ++g) colidx[g] = sc.col(c0 + g);
-  uint32_t xr[GP][F::CB][VX][16];
-  float ncr[GP][F::CB];
-  load_prepared<FMT, GP, VX>(xpf, xncf, a.nb_d, colidx, ch, xr, ncr);
-  __builtin_amdgcn_sched_barrier(0);  // activation loads go out before the weights
+  int u = wave;
+  UnitPos up = unit_pos(u, P, R, geo.rpi);
+  const int ch = li + geo.lpr * up.part;
   const uint32_t coff = (uint32_t)(rg * cpitch + ch * F::CBYTES);
   const uint32_t soff = (uint32_t)(rg * spitch + ch * F::SBYTES);
-  float tot[R][2][GP];
-  unit_rows<FMT, GP, VX, 2, R>(mats, cpitch, spitch, tile * a.rw_gu + up.rloc_u, geo.rpi,
-                               coff, soff, xr, ncr, tot);
-  const int P = geo.tpl, rw = a.rw_gu;
+  uint32_t cw[R][2][F::CW], sw[R][2];
+  unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cw, sw);
+  uint32_t xr[GP][F::CB][VX][16];
+  float ncr[GP][F::CB];
+  load_prepared_x<FMT, GP, VX>(a, colidx, ch, xr, ncr);
+  const uint32_t one = one_one_vgpr();
+  while (true) {
+    float tot[R][2][GP];
+    unit_compute<FMT, GP, VX, 2, R>(cw, sw, xr, ncr, one, tot);
 #pragma unroll
-  for (int i = 0; i < R; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int g = 0; g < GP; ++g) {
-        const float v = group_sum(tot[i][m][g], geo.lpr);
-        if (li == 0)
-          gup[((m * P + up.part) * kQMax + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i] = v;
-      }
+        for (int g = 0; g < GP; ++g) {
+          const float v = group_sum(tot[i][m][g], geo.lpr);
+          if (li == 0)
+            gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i] = v;
+        }
+    u += waves;
+    if (u >= units) break;
+    up = unit_pos(u, P, R, geo.rpi);
+    unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cw, sw);
+  }
 }
 
-template <int FMT, int G, int VX, int R>
+// h of one gate/up tile of a slot for all of the slot's columns, into
+// hs[c][row] in LDS.
+template <int FMT, int G, int VX>
 __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc,
-                                            const ExpertDesc &ed, float *hs, float *gup) {
+                                            const ExpertDesc &ed, int tile, float *hs,
+                                            float *gup) {
+  constexpr int R = unit_rows_for(FMT, G);
   const Geo geo = a.geo_gu[FMT];
   const uint32_t cpitch = (uint32_t)(a.d / 32) * code_bytes(FMT);
   const uint32_t spitch = (uint32_t)(a.d / 32) * scale_bytes(FMT);
   const MatPtr mats[2] = {
       {make_rsrc(a.image + ed.codes[0], a.f * cpitch), make_rsrc(a.image + ed.scales[0], a.f * spitch)},
       {make_rsrc(a.image + ed.codes[1], a.f * cpitch), make_rsrc(a.image + ed.scales[1], a.f * spitch)}};
-  const int P = geo.tpl, rw = a.rw_gu;
+  const int P = geo.tpl, rw = a.rw_gu, q = a.q;
   const int units = rw / (R * geo.rpi) * P;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = uniform(threadIdx.x >> 6);
   const int waves = blockDim.x >> 6;
-  const float A = code_gain(FMT);
-  for (int c0 = 0; c0 < sc.ncols; c0 += G) {
-    const int gc = (G == 2 && sc.ncols - c0 >= 2) ? 2 : 1;
-    for (int u = wave; u < units; u += waves) {
-      const UnitPos up = unit_pos(u, P, R, geo.rpi);
-      if (gc == 2)
-        gateup_unit<FMT, (G == 2 ? 2 : 1), VX, R>(a, sc, c0, geo, up, blockIdx.x, mats, cpitch, spitch, gup);
-      else
-        gateup_unit<FMT, 1, VX, R>(a, sc, c0, geo, up, blockIdx.x, mats, cpitch, spitch, gup);
+  // FP2 chunks hold two blocks: with fp32 activations (hi + lo) two-column
+  // passes would need 128 registers of activations, so those take one
+  constexpr int GD = (FMT == RFPX_FP2 && VX == 2) ? 1 : G;
+  for (int c0 = 0; c0 < sc.ncols; c0 += GD) {
+    const int gc = (GD == 2 && sc.ncols - c0 >= 2) ? 2 : 1;
+    if (wave < units) {
+      if constexpr (GD == 2) {
+        if (gc == 2)
+          gateup_pass<FMT, 2, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
+        else
+          gateup_pass<FMT, 1, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
+      } else {
+        gateup_pass<FMT, 1, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
+      }
     }
     __syncthreads();
     for (int it = threadIdx.x; it < gc * rw; it += blockDim.x) {
       const int c = c0 + it / rw, row = it % rw;
       float g = 0.f, uu = 0.f;
       for (int pp = 0; pp < P; ++pp) {
-        g += gup[((0 * P + pp) * kQMax + c) * rw + row];
-        uu += gup[((1 * P + pp) * kQMax + c) * rw + row];
+        g += gup[((0 * P + pp) * q + c) * rw + row];
+        uu += gup[((1 * P + pp) * q + c) * rw + row];
       }
-      hs[c * rw + row] = silu(A * g) * (A * uu);
+      hs[c * rw + row] = silu(g) * uu;
     }
     __syncthreads();
   }
@@ -322,28 +383,66 @@ __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc
 // and its share of the block's accumulator start.
 template <int FMT_DN>
 __device__ __forceinline__ float prep_h_pair(const float *hblk, int p, uint32_t *dst) {
-  int lo, hi;
-  float slo, shi;
-  pair_def<FMT_DN>(p, lo, hi, slo, shi);
+  int lo, hi, klo, khi;
+  pair_def<FMT_DN>(p, lo, hi, klo, khi);
   const float vl = hblk[lo], vh = hblk[hi];
-  const uint32_t lh = float_to_bf16_rne(vl), hh = float_to_bf16_rne(vh);
-  const uint32_t ll = float_to_bf16_rne(vl - bf16_bits_to_float(lh));
-  const uint32_t hl = float_to_bf16_rne(vh - bf16_bits_to_float(hh));
-  dst[p] = pair_word<FMT_DN>(lh, hh, slo, shi);
-  dst[16 + p] = pair_word<FMT_DN>(ll, hl, slo, shi);
-  return pair_nc<FMT_DN>(bf16_bits_to_float(lh), bf16_bits_to_float(hh), slo, shi) +
-         pair_nc<FMT_DN>(bf16_bits_to_float(ll), bf16_bits_to_float(hl), slo, shi);
+  const float lh = bf16_bits_to_float(float_to_bf16_rne(vl));
+  const float hh = bf16_bits_to_float(float_to_bf16_rne(vh));
+  const float ll = bf16_bits_to_float(float_to_bf16_rne(vl - lh));
+  const float hl = bf16_bits_to_float(float_to_bf16_rne(vh - hh));
+  float nc = 0.f;
+  dst[p] = prepared_pair<FMT_DN>(lh, hh, klo, khi, &nc);
+  dst[16 + p] = prepared_pair<FMT_DN>(ll, hl, klo, khi, &nc);
+  return nc;
 }
 
-template <int G, int VX, int R>
+// Gate/up tile `tile` of slot `slot`, then h of the tile prepared for the
+// slot's down matrix: 16 threads per (column, block), one pair word each;
+// the block's accumulator start is the sum of the 16 shares (aligned groups
+// of 16 lanes).  LDS: hs [q][rw], then gup [2][2][q][rw].
+template <int G, int VX>
+__device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, int slot,
+                                          int tile, float *lds) {
+  float *hs = lds;
+  float *gup = lds + a.q * a.rw_gu;
+  const ExpertDesc ed = load_desc(a.image, sc.expert);
+  const int fmt = ed.fmt[0];
+  if (fmt == RFPX_FP2) gateup_tile<RFPX_FP2, G, VX>(a, sc, ed, tile, hs, gup);
+  else if (fmt == RFPX_FP3) gateup_tile<RFPX_FP3, G, VX>(a, sc, ed, tile, hs, gup);
+  else gateup_tile<RFPX_FP4, G, VX>(a, sc, ed, tile, hs, gup);
+  const int nbt = a.rw_gu / 32;
+  const int fdn = ed.fmt[2];
+  const int nitems = sc.ncols * nbt * 16;
+  for (int base = 0; base < nitems; base += blockDim.x) {
+    const int it = base + threadIdx.x;
+    float share = 0.f;
+    size_t item = 0;
+    if (it < nitems) {
+      const int p = it & 15, cb = it >> 4;
+      const int ci = cb / nbt, bt = cb % nbt;
+      item = ((size_t)slot * a.q + ci) * a.nb_f + tile * nbt + bt;
+      const float *hblk = hs + ci * a.rw_gu + 32 * bt;
+      uint32_t *dst = a.hp + item * 32;
+      if (fdn == RFPX_FP2) share = prep_h_pair<RFPX_FP2>(hblk, p, dst);
+      else if (fdn == RFPX_FP3) share = prep_h_pair<RFPX_FP3>(hblk, p, dst);
+      else share = prep_h_pair<RFPX_FP4>(hblk, p, dst);
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
+    if (it < nitems && (it & 15) == 0) a.hnc[item] = share;
+  }
+}
+
+// Gate/up tile blockIdx.x of slot blockIdx.y.  Slot 0 is the shared expert
+// (every column, weight 1, no routing); routed slots run the routing step
+// in LDS first.
+template <int G, int VX>
 __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
   const int slot = blockIdx.y;
   __shared__ RouteLds rs;
-  extern __shared__ float lds[];  // hs [kQMax][rw], then gup [2][2][kQMax][rw]
-  float *hs = lds;
-  float *gup = lds + kQMax * a.rw_gu;
+  extern __shared__ float lds[];
   SlotCols sc;
-  if (slot == 0) {  // the shared expert: every column, weight 1, no routing
+  if (slot == 0) {
     if (threadIdx.x < kQMax) {
       rs.cols[0][threadIdx.x] = threadIdx.x;
       rs.w[0][threadIdx.x] = 1.f;
@@ -360,148 +459,141 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
   }
   sc.cols = rs.cols[slot];
   sc.w = rs.w[slot];
-  const ExpertDesc ed = load_desc(a.image, sc.expert);
-  const int fmt = ed.fmt[0];
-  if (fmt == RFPX_FP2) gateup_tile<RFPX_FP2, G, VX, R>(a, sc, ed, hs, gup);
-  else if (fmt == RFPX_FP3) gateup_tile<RFPX_FP3, G, VX, R>(a, sc, ed, hs, gup);
-  else gateup_tile<RFPX_FP4, G, VX, R>(a, sc, ed, hs, gup);
-  // prepare h of this tile for the down matrix: 16 threads per (column,
-  // block), one pair word each; the block's accumulator start is the sum of
-  // the 16 shares (aligned groups of 16 lanes)
-  const int nbt = a.rw_gu / 32;
-  const int fdn = ed.fmt[2];
-  const int nitems = sc.ncols * nbt * 16;
-  for (int base = 0; base < nitems; base += blockDim.x) {
-    const int it = base + threadIdx.x;
-    float share = 0.f;
-    size_t item = 0;
-    if (it < nitems) {
-      const int p = it & 15, cb = it >> 4;
-      const int ci = cb / nbt, bt = cb % nbt;
-      item = ((size_t)slot * a.q + ci) * a.nb_f + blockIdx.x * nbt + bt;
-      const float *hblk = hs + ci * a.rw_gu + 32 * bt;
-      uint32_t *dst = a.hp + item * 32;
-      if (fdn == RFPX_FP2) share = prep_h_pair<RFPX_FP2>(hblk, p, dst);
-      else if (fdn == RFPX_FP3) share = prep_h_pair<RFPX_FP3>(hblk, p, dst);
-      else share = prep_h_pair<RFPX_FP4>(hblk, p, dst);
-    }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
-    if (it < nitems && (it & 15) == 0) a.hnc[item] = share;
-  }
+  gateup_wg<G, VX>(a, sc, slot, blockIdx.x, lds);
 }
 
 // ----------------------------------------------------------------- down
 
+// One unit of one slot's down matrix for GP compact columns c0..: the
+// weighted row results are added into the wave's own accumulator rows
+// accw[column][row] (LDS, one writer lane per entry).
 template <int FMT, int GP, int R>
-__device__ __forceinline__ void down_unit(const ExpArgs &a, int slot, int c0, const Geo &geo,
-                                          const UnitPos &up, int tile, const MatPtr (&mats)[1],
-                                          uint32_t cpitch, uint32_t spitch,
-                                          float *op /* [P][kQMax][rw] */) {
+__device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, int slot, int c0,
+                                          const Geo &geo, const UnitPos &up, int r0,
+                                          const MatPtr (&mats)[1], uint32_t cpitch,
+                                          uint32_t spitch, float *accw) {
   using F = Fmt<FMT>;
   const int lane = threadIdx.x & 63;
   const int rg = lane / geo.lpr, li = lane % geo.lpr;
   const int ch = li + geo.lpr * up.part;
-  const uint32_t *hps = a.hp + (size_t)slot * a.q * a.nb_f * 32;
-  const float *hncs = a.hnc + (size_t)slot * a.q * a.nb_f;
-  int colidx[GP];
-#pragma unroll
-  for (int g = 0; g < GP; ++g) colidx[g] = c0 + g;  // compact column index
-  uint32_t xr[GP][F::CB][2][16];
-  float ncr[GP][F::CB];
-  load_prepared<FMT, GP, 2>(hps, hncs, a.nb_f, colidx, ch, xr, ncr);
-  __builtin_amdgcn_sched_barrier(0);  // h loads go out before the weights
   const uint32_t coff = (uint32_t)(rg * cpitch + ch * F::CBYTES);
   const uint32_t soff = (uint32_t)(rg * spitch + ch * F::SBYTES);
+  uint32_t cw[R][1][F::CW], sw[R][1];
+  unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + up.rloc_u, geo.rpi, coff, soff, cw, sw);
+  const uint32_t *hps = a.hp + (size_t)slot * a.q * a.nb_f * 32;
+  const float *hncs = a.hnc + (size_t)slot * a.q * a.nb_f;
+  uint32_t xr[GP][F::CB][2][16];
+  float ncr[GP][F::CB];
+  load_prepared_h<FMT, GP>(hps, hncs, a.nb_f, c0, ch, xr, ncr);
   float to[R][1][GP];
-  unit_rows<FMT, GP, 2, 1, R>(mats, cpitch, spitch, tile * a.rw_dn + up.rloc_u, geo.rpi,
-                              coff, soff, xr, ncr, to);
+  unit_compute<FMT, GP, 2, 1, R>(cw, sw, xr, ncr, one_one_vgpr(), to);
   const int rw = a.rw_dn;
 #pragma unroll
-  for (int i = 0; i < R; ++i)
+  for (int g = 0; g < GP; ++g) {
+    const int col = sc.col(c0 + g);
+    const float wA = sc.weight(c0 + g);
 #pragma unroll
-    for (int g = 0; g < GP; ++g) {
+    for (int i = 0; i < R; ++i) {
       const float v = group_sum(to[i][0][g], geo.lpr);
-      if (li == 0) op[(up.part * kQMax + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i] = v;
+      if (li == 0) accw[col * rw + up.rloc_u + rg + geo.rpi * i] += wA * v;
     }
+  }
 }
 
-template <int FMT, int G, int R>
-__device__ __forceinline__ void down_tile(const ExpArgs &a, const SlotCols &sc, int slot,
-                                          const ExpertDesc &ed, float *op) {
+// The units of one slot that fall to this wave: units are dealt to the
+// waves round-robin in slot order (`item` counts the units dealt so far).
+template <int FMT, int G>
+__device__ __forceinline__ void down_slot(const ExpArgs &a, const SlotCols &sc, int slot,
+                                          const ExpertDesc &ed, int r0, int wave, int waves,
+                                          int &item, float *accw) {
+  constexpr int R = unit_rows_for(FMT, G);
   const Geo geo = a.geo_dn[FMT];
   const uint32_t cpitch = (uint32_t)(a.f / 32) * code_bytes(FMT);
   const uint32_t spitch = (uint32_t)(a.f / 32) * scale_bytes(FMT);
   const MatPtr mats[1] = {
       {make_rsrc(a.image + ed.codes[2], a.d * cpitch), make_rsrc(a.image + ed.scales[2], a.d * spitch)}};
-  const int P = geo.tpl, rw = a.rw_dn;
-  const int units = rw / (R * geo.rpi) * P;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int waves = blockDim.x >> 6;
-  const float A = code_gain(FMT);
-  for (int c0 = 0; c0 < sc.ncols; c0 += G) {
-    const int gc = (G == 2 && sc.ncols - c0 >= 2) ? 2 : 1;
-    for (int u = wave; u < units; u += waves) {
-      const UnitPos up = unit_pos(u, P, R, geo.rpi);
-      if (gc == 2)
-        down_unit<FMT, (G == 2 ? 2 : 1), R>(a, slot, c0, geo, up, blockIdx.x, mats, cpitch, spitch, op);
-      else
-        down_unit<FMT, 1, R>(a, slot, c0, geo, up, blockIdx.x, mats, cpitch, spitch, op);
+  // FP2 chunks hold two blocks, so two-column passes would need 128
+  // registers of h: FP2 down matrices take one column per pass
+  constexpr int GD = FMT == RFPX_FP2 ? 1 : G;
+  const int P = geo.tpl;
+  const int units = a.rw_dn / (R * geo.rpi) * P;
+  for (int u = 0; u < units; ++u, ++item) {
+    if (item % waves != wave) continue;
+    const UnitPos up = unit_pos(u, P, R, geo.rpi);
+    for (int c0 = 0; c0 < sc.ncols; c0 += GD) {
+      if constexpr (GD == 2) {
+        if (sc.ncols - c0 >= 2)
+          down_unit<FMT, 2, R>(a, sc, slot, c0, geo, up, r0, mats, cpitch, spitch, accw);
+        else
+          down_unit<FMT, 1, R>(a, sc, slot, c0, geo, up, r0, mats, cpitch, spitch, accw);
+      } else {
+        down_unit<FMT, 1, R>(a, sc, slot, c0, geo, up, r0, mats, cpitch, spitch, accw);
+      }
     }
-    __syncthreads();
-    for (int it = threadIdx.x; it < gc * rw; it += blockDim.x) {
-      const int ci = c0 + it / rw, row = it % rw;
-      float o = 0.f;
-      for (int pp = 0; pp < P; ++pp) o += op[(pp * kQMax + ci) * rw + row];
-      a.part[((size_t)slot * a.q + ci) * a.d + blockIdx.x * rw + row] = sc.weight(ci) * (A * o);
-    }
-    __syncthreads();
   }
 }
 
-__device__ __forceinline__ SlotCols slot_from_table(const RouteTable *rt, int slot) {
-  SlotCols sc;
-  sc.expert = uniform(rt->expert[slot]);
-  sc.ncols = uniform(rt->ncols[slot]);
-  sc.cols = rt->cols[slot];
-  sc.w = rt->w[slot];
-  return sc;
-}
-
-template <int G, int R>
+// Down rows [r0, r0 + RW_DN) of every slot, combined into y.  The slot table
+// is copied to LDS first; each wave accumulates its units into its own LDS
+// rows, and the epilogue sums the waves in a fixed order, so y is the same
+// bit for bit from run to run.
+template <int G>
 __global__ __launch_bounds__(512) void k_down(ExpArgs a) {
-  const int slot = blockIdx.y;
-  if (slot >= uniform(a.rt->nslots)) return;
-  extern __shared__ float op[];  // [2][kQMax][rw]
-  const SlotCols sc = slot_from_table(a.rt, slot);
-  const ExpertDesc ed = load_desc(a.image, sc.expert);
-  const int fmt = ed.fmt[2];
-  if (fmt == RFPX_FP2) down_tile<RFPX_FP2, G, R>(a, sc, slot, ed, op);
-  else if (fmt == RFPX_FP3) down_tile<RFPX_FP3, G, R>(a, sc, slot, ed, op);
-  else down_tile<RFPX_FP4, G, R>(a, sc, slot, ed, op);
-}
-
-// y[c][i] = sum over slots s that hold column c, in slot order, of the
-// weighted partials.
-__global__ __launch_bounds__(256) void k_combine(ExpArgs a) {
-  const int it = blockIdx.x * blockDim.x + threadIdx.x;
-  if (it >= a.q * a.d) return;
-  const int c = it / a.d, row = it % a.d;
-  const RouteTable *rt = a.rt;
-  const int nslots = rt->nslots;
-  float acc = 0.f;
-  for (int s = 0; s < nslots; ++s) {
-    const uint32_t m = rt->mask[s];
-    if (!((m >> c) & 1u)) continue;
-    const int ci = __popc(m & ((1u << c) - 1u));
-    acc += a.part[((size_t)s * a.q + ci) * a.d + row];
+  __shared__ int32_t t_ncols[kMaxSlots];
+  __shared__ int32_t t_cols[kMaxSlots][kQMax];
+  __shared__ float t_w[kMaxSlots][kQMax];
+  __shared__ uint64_t t_codes[kMaxSlots], t_scales[kMaxSlots];
+  __shared__ int32_t t_fmt[kMaxSlots];
+  extern __shared__ float acc[];  // [waves][q][rw]
+  const int rw = a.rw_dn, q = a.q;
+  const int waves = blockDim.x >> 6;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int nslots = uniform(a.rt->nslots);
+  for (int i = threadIdx.x; i < waves * q * rw; i += blockDim.x) acc[i] = 0.f;
+  // the slot table and each slot's down-matrix entry of the image table,
+  // all loads in flight together
+  for (int i = threadIdx.x; i < nslots * (kQMax + 1); i += blockDim.x) {
+    const int s = i / (kQMax + 1), j = i % (kQMax + 1);
+    if (j == kQMax) {
+      const ExpertDesc *t =
+          reinterpret_cast<const ExpertDesc *>(a.image + kImgTable) + a.rt->expert[s];
+      t_ncols[s] = a.rt->ncols[s];
+      t_codes[s] = t->codes[2];
+      t_scales[s] = t->scales[2];
+      t_fmt[s] = t->fmt[2];
+    } else {
+      t_cols[s][j] = a.rt->cols[s][j];
+      t_w[s][j] = a.rt->w[s][j];
+    }
   }
-  a.y[it] = acc;
+  __syncthreads();
+  const int r0 = blockIdx.x * rw;
+  float *accw = acc + wave * q * rw;
+  int item = 0;
+  for (int s = 0; s < nslots; ++s) {
+    SlotCols sc;
+    sc.expert = -1;  // not needed: the down entry is in LDS
+    sc.ncols = uniform(t_ncols[s]);
+    sc.cols = t_cols[s];
+    sc.w = t_w[s];
+    ExpertDesc ed{};
+    ed.codes[2] = uniform64(t_codes[s]);
+    ed.scales[2] = uniform64(t_scales[s]);
+    const int fmt = uniform(t_fmt[s]);
+    if (fmt == RFPX_FP2) down_slot<RFPX_FP2, G>(a, sc, s, ed, r0, wave, waves, item, accw);
+    else if (fmt == RFPX_FP3) down_slot<RFPX_FP3, G>(a, sc, s, ed, r0, wave, waves, item, accw);
+    else down_slot<RFPX_FP4, G>(a, sc, s, ed, r0, wave, waves, item, accw);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < q * rw; i += blockDim.x) {
+    const int c = i / rw, row = i % rw;
+    float v = 0.f;
+    for (int w = 0; w < waves; ++w) v += acc[(w * q + c) * rw + row];
+    a.y[(size_t)c * a.d + r0 + row] = v;
+  }
 }
 
-}  // namespace
-
-hipError_t launch_experts(const ForwardPlan &p) {
+ExpArgs make_args(const ForwardPlan &p) {
   ExpArgs a{};
   a.image = p.image;
   a.rt = reinterpret_cast<RouteTable *>(p.ws + p.wl.route);
@@ -510,7 +602,6 @@ hipError_t launch_experts(const ForwardPlan &p) {
   a.xnc = reinterpret_cast<const float *>(p.ws + p.wl.xnc);
   a.hp = reinterpret_cast<uint32_t *>(p.ws + p.wl.hp);
   a.hnc = reinterpret_cast<float *>(p.ws + p.wl.hnc);
-  a.part = reinterpret_cast<float *>(p.ws + p.wl.part);
   a.y = p.y;
   a.d = p.d;
   a.f = p.f;
@@ -523,31 +614,33 @@ hipError_t launch_experts(const ForwardPlan &p) {
   }
   a.rw_gu = p.rw_gu;
   a.rw_dn = p.rw_dn;
-  const int slots = p.wl.max_slots;
-  dim3 ggu(p.f / p.rw_gu, slots), gdn(p.d / p.rw_dn, slots);
-  const size_t lds_gu = (size_t)5 * kQMax * p.rw_gu * sizeof(float);  // hs + gup
-  const size_t lds_dn = (size_t)2 * kQMax * p.rw_dn * sizeof(float);  // op
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_experts(const ForwardPlan &p) {
+  const ExpArgs a = make_args(p);
+  const dim3 ggu(p.f / p.rw_gu, p.wl.max_slots), gdn(p.d / p.rw_dn);
+  const size_t lds_gu = (size_t)5 * p.q * p.rw_gu * sizeof(float);        // hs + gup
+  const size_t lds_dn = (size_t)p.wmax * p.q * p.rw_dn * sizeof(float);   // acc
+  const unsigned nt = 64 * p.wmax;
   const bool bf = p.xtype == RFPX_X_BF16;
   hipEvent_t *ev = (hipEvent_t *)p.events;
-  const unsigned nt = 64 * p.wmax;
   if (p.g == 1) {
-    if (bf) k_gateup<1, 1, 4><<<ggu, nt, lds_gu, p.stream>>>(a);
-    else k_gateup<1, 2, 4><<<ggu, nt, lds_gu, p.stream>>>(a);
+    if (bf) k_gateup<1, 1><<<ggu, nt, lds_gu, p.stream>>>(a);
+    else k_gateup<1, 2><<<ggu, nt, lds_gu, p.stream>>>(a);
   } else {
-    if (bf) k_gateup<2, 1, 4><<<ggu, nt, lds_gu, p.stream>>>(a);
-    else k_gateup<2, 2, 4><<<ggu, nt, lds_gu, p.stream>>>(a);
+    if (bf) k_gateup<2, 1><<<ggu, nt, lds_gu, p.stream>>>(a);
+    else k_gateup<2, 2><<<ggu, nt, lds_gu, p.stream>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], p.stream);
   if (e != hipSuccess) return e;
-  if (p.g == 1) k_down<1, 4><<<gdn, nt, lds_dn, p.stream>>>(a);
-  else k_down<2, 4><<<gdn, nt, lds_dn, p.stream>>>(a);
+  if (p.g == 1) k_down<1><<<gdn, nt, lds_dn, p.stream>>>(a);
+  else k_down<2><<<gdn, nt, lds_dn, p.stream>>>(a);
   e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[3], p.stream);
-  if (e != hipSuccess) return e;
-  k_combine<<<(p.q * p.d + 255) / 256, 256, 0, p.stream>>>(a);
-  e = hipGetLastError();
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[4], p.stream);
   return e;
 }
 

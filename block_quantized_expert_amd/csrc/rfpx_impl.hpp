@@ -4,29 +4,35 @@
 //
 // Block decode on gfx950.  The expert products run on v_dot2c_f32_bf16
 // (two bf16 products added into an fp32 accumulator per lane per issue).
-// A packed code c is turned into the bf16 value 1 + c/2^k by masking it
-// into the mantissa of 1.0 (0x3F80): one shift (or funnel shift) and one
-// and-or per pair of codes, i.e. about one VALU op per weight, shared by all
-// columns.  The constant part of 1 + c/2^k and the code offset (1.5, 3.5,
-// 7.5) are folded into a per-block, per-column accumulator start value
-// computed once from the activations ("prepared" activations below), so
-//      sum_j (c_j - offset) x_j  =  A * (nc + sum_pairs dot2(v, xpair))
-// with A = 8 (FP2, FP3) or 16 (FP4).  v and the bf16 activations are exact,
-// each bf16 product is exact in fp32, so the only rounding is fp32
-// accumulation.
+// A packed code c is turned into a bf16 value by masking it into the
+// mantissa of 1.0 (0x3F80): a code whose lowest bit lands at mantissa bit k
+// gives 1 + c * 2^(k-7).  One v_and_or_b32 builds a pair word (two codes,
+// one per bf16 half) from a shifted copy of the code dword, and one shift
+// serves several pairs, so the decode costs 0.6 (FP2) to 1 (FP3) VALU op
+// per weight, shared by all columns.  The factor 2^(7-k) of each code and
+// the code offset (1.5, 3.5, 7.5) are folded into "prepared" activations,
+// computed once per step: the activation of a code at position k is stored
+// times 2^(7-k) (exact), and each block's accumulator starts at
+// -sum (2^(7-k) + offset) * x, so that
+//      sum_j (c_j - offset) x_j  =  start + sum_pairs dot2(v, xpair).
+// v and the bf16 activations are exact and each bf16 product is exact in
+// fp32, so the only rounding is fp32 accumulation.
 //
-// Pairings (lo code, hi code) of the 16 pairs of one block, and where each
-// code lands in the 32-bit pair word (bf16 lo in bits 0..15, hi in 16..31):
-//   FP2  pair 8t+a (t<2, a<8): codes (16t+a, 16t+a+8) -> bits 4-5 / 20-21,
-//        v = 1 + c/8 on both halves.  Window: dword t >> (2a-4).
-//   FP4  pair 4t+a (t<4, a<4): codes (8t+a, 8t+a+4)   -> bits 3-6 / 19-22,
-//        v = 1 + c/16.  Window: dword t >> (4a-3).
-//   FP3  pairs 0..9: codes (lo, lo+5), lo in {0..4, 10..14}; lo at bits 4-6
-//        (v = 1 + c/8), hi at bits 19-21 (v = 1 + c/16); the activation of
-//        the hi code is stored doubled.  Pairs 10..15: codes (lo, lo+6), lo
-//        in 20..25; lo at bits 2-4 (v = 1 + c/32, activation stored x4), hi
-//        at bits 20-22 (v = 1 + c/8).  Window: bits 3lo-4 (resp. 3lo-2) of
-//        the 96-bit code word, taken with one v_alignbit_b32.
+// Pairings (lo code, hi code) of the 16 pairs of one block (bf16 lo half in
+// bits 0..15 of the pair word, hi half in 16..31), with the code's mantissa
+// position k:
+//   FP2  code dword t (t < 2) holds codes 16t..16t+15; pair 8t+i joins
+//        codes 16t+i and 16t+i+8, taken from the dword shifted right by
+//        0 (i = 0..2), 6 (i = 3..5) or 12 (i = 6, 7); k = 0, 2, 4, 0, 2, 4,
+//        0, 2 for i = 0..7, the same in both halves.
+//   FP4  code dword t (t < 4) holds codes 8t..8t+7; pair 4t+i joins codes
+//        8t+i and 8t+i+4; i = 0 at k = 0 (no shift), i = 1, 2, 3 at k = 3
+//        (shift right 1, 5, 9).
+//   FP3  pairs 0..9: codes (lo, lo+5), lo in {0..4, 10..14}; lo at bits
+//        4-6 (k = 4), hi at bits 19-21 (k = 3).  Pairs 10..15: codes
+//        (lo, lo+6), lo in 20..25; lo at bits 2-4 (k = 2), hi at bits 20-22
+//        (k = 4).  Window: bits 3lo-4 (resp. 3lo-2) of the 96-bit code word,
+//        taken with one v_alignbit_b32.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,7 +48,6 @@ constexpr int kEMax = RFPX_E_MAX;
 constexpr int kMaxSlots = kQMax * kKMax + 1;  // routed unique experts + shared
 constexpr uint32_t kMagic = 0x58504652u;      // "RFPX"
 constexpr uint32_t kVersion = 1;
-constexpr uint32_t kOneOne = 0x3F803F80u;     // bf16 pair (1.0, 1.0)
 
 __host__ __device__ constexpr int code_bytes(int fmt) {
   return fmt == RFPX_FP2 ? 8 : fmt == RFPX_FP3 ? 12 : fmt == RFPX_FP4 ? 16 : 0;
@@ -61,11 +66,6 @@ __host__ __device__ constexpr bool valid_fmt(int fmt) {
 __host__ __device__ constexpr int chunk_blocks(int fmt) {
   return fmt == RFPX_FP2 ? 2 : 1;
 }
-// A in  sum (c - offset) x = A * acc.
-__host__ __device__ constexpr float code_gain(int fmt) {
-  return fmt == RFPX_FP4 ? 16.f : 8.f;
-}
-
 // ----------------------------------------------------------------- image
 
 struct ImageHeader {
@@ -136,13 +136,20 @@ struct WsLayout {
   size_t route;     // RouteTable
   size_t scores;    // fp32 [q][E]
   size_t xp;        // u32  [3 fmts][q][nb_d][vx][16]  prepared activations
-  size_t xnc;       // fp32 [3][q][nb_d]
+  size_t xnc;       // fp32 [3][q][nb_d]               their accumulator starts
   size_t hp;        // u32  [slots][q][nb_f][2][16]    prepared h (hi, lo)
   size_t hnc;       // fp32 [slots][q][nb_f]
-  size_t part;      // fp32 [slots][q][d]              weighted partial outputs
   size_t total;
   int max_slots;
 };
+
+// Rows per wave unit of the expert kernels: one-column passes of FP3/FP4
+// take 8 rows (a 64-lane row of FP4 codes is 1 KiB, so 8 rows of gate and
+// up keep 17 KiB in flight per wave); everything else takes 4, which keeps
+// two-column passes within the register budget of two waves per SIMD.
+__host__ __device__ constexpr int unit_rows_for(int fmt, int g) {
+  return (g == 1 && fmt != RFPX_FP2) ? 8 : 4;
+}
 
 // ------------------------------------------------------------ device side
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
@@ -164,127 +171,143 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
                                          false);
 }
 
-// Decode the codes of one block into its 16 bf16 pair words (see header).
-// `w` holds the block's code dwords: 2 (FP2), 3 (FP3) or 4 (FP4).
+// (x & m) | o.  With the OR constant held in a vector register (o from
+// one_one_vgpr) the compiler emits one v_and_or_b32 per pair word; with two
+// literal constants it emits a separate AND and OR.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t o) {
+  return (x & m) | o;
+}
+// The bf16 pair (1.0, 1.0) in a vector register the compiler cannot fold
+// back into a literal.
+__device__ __forceinline__ uint32_t one_one_vgpr() {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, 0x3f803f80" : "=v"(r));
+  return r;
+}
+
+// Decode the codes of one block into its 16 bf16 pair words (see the header
+// comment for the pairings).  `w` holds the block's code dwords: 2 (FP2),
+// 3 (FP3) or 4 (FP4); `one` is one_one_vgpr().
 template <int FMT>
-__device__ __forceinline__ void decode_pairs(const uint32_t *w, uint32_t *p);
+__device__ __forceinline__ void decode_pairs(const uint32_t *w, uint32_t *p, uint32_t one);
 
 template <>
-__device__ __forceinline__ void decode_pairs<RFPX_FP2>(const uint32_t *w, uint32_t *p) {
-  constexpr uint32_t M = 0x00300030u;
+__device__ __forceinline__ void decode_pairs<RFPX_FP2>(const uint32_t *w, uint32_t *p,
+                                                       uint32_t one) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    uint32_t v = w[t];
-    p[8 * t + 0] = ((v << 4) & M) | kOneOne;
-    p[8 * t + 1] = ((v << 2) & M) | kOneOne;
-    p[8 * t + 2] = (v & M) | kOneOne;
-    p[8 * t + 3] = ((v >> 2) & M) | kOneOne;
-    p[8 * t + 4] = ((v >> 4) & M) | kOneOne;
-    p[8 * t + 5] = ((v >> 6) & M) | kOneOne;
-    p[8 * t + 6] = ((v >> 8) & M) | kOneOne;
-    p[8 * t + 7] = ((v >> 10) & M) | kOneOne;
+    const uint32_t v = w[t], v6 = v >> 6, v12 = v >> 12;
+    p[8 * t + 0] = and_or(v, 0x00030003u, one);
+    p[8 * t + 1] = and_or(v, 0x000C000Cu, one);
+    p[8 * t + 2] = and_or(v, 0x00300030u, one);
+    p[8 * t + 3] = and_or(v6, 0x00030003u, one);
+    p[8 * t + 4] = and_or(v6, 0x000C000Cu, one);
+    p[8 * t + 5] = and_or(v6, 0x00300030u, one);
+    p[8 * t + 6] = and_or(v12, 0x00030003u, one);
+    p[8 * t + 7] = and_or(v12, 0x000C000Cu, one);
   }
 }
 
 template <>
-__device__ __forceinline__ void decode_pairs<RFPX_FP4>(const uint32_t *w, uint32_t *p) {
-  constexpr uint32_t M = 0x00780078u;
+__device__ __forceinline__ void decode_pairs<RFPX_FP4>(const uint32_t *w, uint32_t *p,
+                                                       uint32_t one) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    uint32_t v = w[t];
-    p[4 * t + 0] = ((v << 3) & M) | kOneOne;
-    p[4 * t + 1] = ((v >> 1) & M) | kOneOne;
-    p[4 * t + 2] = ((v >> 5) & M) | kOneOne;
-    p[4 * t + 3] = ((v >> 9) & M) | kOneOne;
+    const uint32_t v = w[t];
+    p[4 * t + 0] = and_or(v, 0x000F000Fu, one);
+    p[4 * t + 1] = and_or(v >> 1, 0x00780078u, one);
+    p[4 * t + 2] = and_or(v >> 5, 0x00780078u, one);
+    p[4 * t + 3] = and_or(v >> 9, 0x00780078u, one);
   }
 }
 
 template <>
-__device__ __forceinline__ void decode_pairs<RFPX_FP3>(const uint32_t *w, uint32_t *p) {
+__device__ __forceinline__ void decode_pairs<RFPX_FP3>(const uint32_t *w, uint32_t *p,
+                                                       uint32_t one) {
   constexpr uint32_t MA = 0x00380070u;  // lo bits 4-6, hi bits 19-21
   constexpr uint32_t MB = 0x0070001Cu;  // lo bits 2-4, hi bits 20-22
   const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
   // type A, window start 3*lo - 4 for lo = 0,1,2,3,4,10,11,12,13,14
-  p[0] = ((w0 << 4) & MA) | kOneOne;                                 // -4
-  p[1] = ((w0 << 1) & MA) | kOneOne;                                 // -1
-  p[2] = (__builtin_amdgcn_alignbit(w1, w0, 2) & MA) | kOneOne;      // 2
-  p[3] = (__builtin_amdgcn_alignbit(w1, w0, 5) & MA) | kOneOne;      // 5
-  p[4] = (__builtin_amdgcn_alignbit(w1, w0, 8) & MA) | kOneOne;      // 8
-  p[5] = (__builtin_amdgcn_alignbit(w1, w0, 26) & MA) | kOneOne;     // 26
-  p[6] = (__builtin_amdgcn_alignbit(w1, w0, 29) & MA) | kOneOne;     // 29
-  p[7] = (w1 & MA) | kOneOne;                                        // 32
-  p[8] = (__builtin_amdgcn_alignbit(w2, w1, 3) & MA) | kOneOne;      // 35
-  p[9] = (__builtin_amdgcn_alignbit(w2, w1, 6) & MA) | kOneOne;      // 38
+  p[0] = and_or(w0 << 4, MA, one);                                 // -4
+  p[1] = and_or(w0 << 1, MA, one);                                 // -1
+  p[2] = and_or(__builtin_amdgcn_alignbit(w1, w0, 2), MA, one);    // 2
+  p[3] = and_or(__builtin_amdgcn_alignbit(w1, w0, 5), MA, one);    // 5
+  p[4] = and_or(__builtin_amdgcn_alignbit(w1, w0, 8), MA, one);    // 8
+  p[5] = and_or(__builtin_amdgcn_alignbit(w1, w0, 26), MA, one);   // 26
+  p[6] = and_or(__builtin_amdgcn_alignbit(w1, w0, 29), MA, one);   // 29
+  p[7] = and_or(w1, MA, one);                                      // 32
+  p[8] = and_or(__builtin_amdgcn_alignbit(w2, w1, 3), MA, one);    // 35
+  p[9] = and_or(__builtin_amdgcn_alignbit(w2, w1, 6), MA, one);    // 38
   // type B, window start 3*lo - 2 for lo = 20..25
-  p[10] = (__builtin_amdgcn_alignbit(w2, w1, 26) & MB) | kOneOne;    // 58
-  p[11] = (__builtin_amdgcn_alignbit(w2, w1, 29) & MB) | kOneOne;    // 61
-  p[12] = (w2 & MB) | kOneOne;                                       // 64
-  p[13] = ((w2 >> 3) & MB) | kOneOne;                                // 67
-  p[14] = ((w2 >> 6) & MB) | kOneOne;                                // 70
-  p[15] = ((w2 >> 9) & MB) | kOneOne;                                // 73
+  p[10] = and_or(__builtin_amdgcn_alignbit(w2, w1, 26), MB, one);  // 58
+  p[11] = and_or(__builtin_amdgcn_alignbit(w2, w1, 29), MB, one);  // 61
+  p[12] = and_or(w2, MB, one);                                     // 64
+  p[13] = and_or(w2 >> 3, MB, one);                                // 67
+  p[14] = and_or(w2 >> 6, MB, one);                                // 70
+  p[15] = and_or(w2 >> 9, MB, one);                                // 73
 }
 
-// Pair p of a block: the codes (and activations) it joins, the factor each
-// activation is stored with, and its share of the accumulator start nc.
+// Pair p of a block: the codes (and activations) it joins, and the
+// mantissa position k of each code in its bf16 half (the half represents
+// 1 + c * 2^(k-7)).
 template <int FMT>
-__device__ __forceinline__ void pair_def(int p, int &lo, int &hi, float &slo,
-                                         float &shi) {
+__device__ __forceinline__ void pair_def(int p, int &lo, int &hi, int &klo, int &khi) {
   if (FMT == RFPX_FP2) {
-    lo = 16 * (p >> 3) + (p & 7);
+    const int i = p & 7;
+    lo = 16 * (p >> 3) + i;
     hi = lo + 8;
-    slo = shi = 1.f;
+    klo = khi = 2 * (i % 3);  // 0, 2, 4, 0, 2, 4, 0, 2
   } else if (FMT == RFPX_FP4) {
-    lo = 8 * (p >> 2) + (p & 3);
+    const int i = p & 3;
+    lo = 8 * (p >> 2) + i;
     hi = lo + 4;
-    slo = shi = 1.f;
+    klo = khi = i == 0 ? 0 : 3;
   } else if (p < 10) {
     lo = p < 5 ? p : p + 5;  // 0..4, 10..14
     hi = lo + 5;
-    slo = 1.f;
-    shi = 2.f;
+    klo = 4;
+    khi = 3;
   } else {
     lo = 20 + (p - 10);  // 20..25
     hi = lo + 6;
-    slo = 4.f;
-    shi = 1.f;
+    klo = 2;
+    khi = 4;
   }
 }
 
-// nc share of one pair with activations xl, xh (see the header comment):
-// FP2 -(1 + 1.5/8)(xl + xh); FP4 -(1 + 7.5/16)(xl + xh);
-// FP3 -(slo xl + shi xh) - (3.5/8)(xl + xh).
+// Code offset o in w = (c - o) * scale: 1.5, 3.5, 7.5.
 template <int FMT>
-__device__ __forceinline__ float pair_nc(float xl, float xh, float slo, float shi) {
-  if (FMT == RFPX_FP2) return -1.1875f * (xl + xh);
-  if (FMT == RFPX_FP4) return -1.46875f * (xl + xh);
-  return -(slo * xl + shi * xh) - 0.4375f * (xl + xh);
+__device__ __forceinline__ float code_offset() {
+  return FMT == RFPX_FP2 ? 1.5f : FMT == RFPX_FP3 ? 3.5f : 7.5f;
 }
 
-// bf16 pair word of pair p from bf16 bit patterns of its two activations
-// (the factors 2 and 4 are exact exponent increments).
+// A code at mantissa position k stands for 1 + c * 2^(k-7) = 2^(k-7) *
+// (c + 2^(7-k)), so its activation is stored times f = 2^(7-k) (exact) and
+// the block's accumulator starts at -sum (f + o) * x; then
+//   start + sum_pairs dot2(decoded pair, prepared pair) = sum_j (c_j - o) x_j.
+// xl, xh must be bf16 values (their fp32 form); the scaled values are
+// exactly bf16 too, so their top 16 bits are the bf16 patterns.
 template <int FMT>
-__device__ __forceinline__ uint32_t pair_word(uint32_t bl, uint32_t bh, float slo,
-                                              float shi) {
-  if (FMT == RFPX_FP3) {
-    if (slo != 1.f) bl = float_to_bf16_rne(slo * bf16_bits_to_float(bl));
-    if (shi != 1.f) bh = float_to_bf16_rne(shi * bf16_bits_to_float(bh));
-  }
-  return bl | (bh << 16);
+__device__ __forceinline__ uint32_t prepared_pair(float xl, float xh, int klo, int khi,
+                                                  float *nc) {
+  const float flo = (float)(1 << (7 - klo)), fhi = (float)(1 << (7 - khi));
+  const float o = code_offset<FMT>();
+  *nc -= (flo + o) * xl + (fhi + o) * xh;
+  return (__float_as_uint(xl * flo) >> 16) | (__float_as_uint(xh * fhi) & 0xFFFF0000u);
 }
 
-// Prepared activations of one block for one virtual column: the 16 bf16
-// pair words matching decode_pairs<FMT> and the accumulator start nc.  xb[j]
-// are bf16 bit patterns of the block's 32 values.
+// Prepared activations of one block for one virtual column: the 16 pair
+// words matching decode_pairs<FMT> and the accumulator start nc.  xb[j] are
+// bf16 bit patterns of the block's 32 values.
 template <int FMT>
 __device__ __forceinline__ void prep_pairs(const uint32_t *xb, uint32_t *pw, float *nc) {
   float acc = 0.f;
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
-    int lo, hi;
-    float slo, shi;
-    pair_def<FMT>(p, lo, hi, slo, shi);
-    pw[p] = pair_word<FMT>(xb[lo], xb[hi], slo, shi);
-    acc += pair_nc<FMT>(bf16_bits_to_float(xb[lo]), bf16_bits_to_float(xb[hi]), slo, shi);
+    int lo, hi, klo, khi;
+    pair_def<FMT>(p, lo, hi, klo, khi);
+    pw[p] = prepared_pair<FMT>(bf16_bits_to_float(xb[lo]), bf16_bits_to_float(xb[hi]), klo, khi,
+                               &acc);
   }
   *nc = acc;
 }
@@ -343,18 +366,21 @@ struct ForwardPlan {
   float *w_out;
   uint8_t *ws;
   WsLayout wl;
-  unsigned prep_fmts;       // bit f set: gate/up format f is present
+  unsigned gu_fmts;         // bit f set: gate/up format f is present
   unsigned down_fmts;       // bit f set: down format f is present
   Geo geo_gu[5], geo_dn[5];  // indexed by format
   int g;                    // columns per pass of the expert kernels (1, 2)
-  int r;                    // rows per wave
   int wmax;                 // waves per workgroup
   int rw_gu, rw_dn;         // rows per workgroup tile
   bool route_only;
   hipStream_t stream;
-  void *const *events;      // optional: 5 hipEvent_t recorded around launches
+  void *const *events;      // optional: 4 hipEvent_t recorded around launches
 };
+// k_route: router scores and prepared activations; for route_only also
+// k_topk (ids and gating weights for moe_route_topk).
 hipError_t launch_route(const ForwardPlan &p);
+// k_gateup (all slots) and k_down (all slots, with the combine); records
+// events[2] and events[3] when events are given.
 hipError_t launch_experts(const ForwardPlan &p);
 
 }  // namespace rfpx

@@ -1,6 +1,7 @@
-// rfpx_route.hpp -- the in-workgroup routing step shared by k_topk and the
-// gate/up kernel: sorted top-k per column, softmax gating, and the slot
-// table of distinct experts over the q verify columns, all in LDS.
+// rfpx_route.hpp -- routing: the router scores of one expert row, and the
+// in-workgroup routing step shared by k_topk and the routed gate/up kernel
+// (sorted top-k per column, softmax gating, and the slot table of distinct
+// experts over the q verify columns, all in LDS).
 //
 // Routing (page "APU 实现 token 自由…" (ainomam.com), section "Lucebox 的优
 // 化三板斧": TOP-K/ARGSORT kernels on the routing path; page "Lucebox专攻
@@ -43,6 +44,75 @@ struct RouteLds {
 };
 
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Router scores s[c][e] = sum_i Wr[e][i] x[c][i] of one expert e for the q
+// columns, by one workgroup of NT threads: thread t takes float4 groups t,
+// t + NT, ... of the row (d <= 4096), all loads issued before the
+// arithmetic (clamped indices, zeroed after, so no load waits on a branch);
+// the wave sums meet in LDS.
+template <int NT>
+__device__ __forceinline__ void router_row(const float *wr, const void *x, int xtype, int d,
+                                           int E, int q, float *scores, int e) {
+  constexpr int NPT = 4096 / 4 / NT;
+  const int tid = threadIdx.x;
+  const int n4 = d / 4;
+  const float4 *wrow = reinterpret_cast<const float4 *>(wr + (size_t)e * d);
+  float4 w[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int i4 = tid + NT * j;
+    w[j] = wrow[i4 < n4 ? i4 : n4 - 1];
+  }
+#pragma unroll
+  for (int j = 0; j < NPT; ++j)
+    if (tid + NT * j >= n4) w[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[kQMax];
+#pragma unroll
+  for (int c = 0; c < kQMax; ++c) {
+    acc[c] = 0.f;
+    if (c >= q) continue;
+    float4 xv[NPT];
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      const int i4 = min(tid + NT * j, n4 - 1);  // w is zero past n4
+      if (xtype == RFPX_X_BF16) {
+        const uint2 b = reinterpret_cast<const uint2 *>(
+            static_cast<const uint16_t *>(x) + (size_t)c * d)[i4];
+        xv[j] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                            __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+      } else {
+        xv[j] = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (size_t)c * d)[i4];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NPT; ++j) {
+      acc[c] = fmaf(w[j].x, xv[j].x, acc[c]);
+      acc[c] = fmaf(w[j].y, xv[j].y, acc[c]);
+      acc[c] = fmaf(w[j].z, xv[j].z, acc[c]);
+      acc[c] = fmaf(w[j].w, xv[j].w, acc[c]);
+    }
+  }
+  __shared__ float part[NT / 64][kQMax];
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int c = 0; c < kQMax; ++c) {
+    if (c >= q) break;
+    const float s = wave_sum_f32(acc[c]);
+    if (lane == 0) part[wave][c] = s;
+  }
+  __syncthreads();
+  if (tid < q) {
+    float s = 0.f;
+    for (int wv = 0; wv < NT / 64; ++wv) s += part[wv][tid];
+    scores[(size_t)tid * E + e] = s;
+  }
+}
 
 // Order-preserving key of an fp32 score: larger score <=> larger key
 // (-0 is folded into +0 first so that the two compare equal, as floats do).

@@ -180,12 +180,12 @@ rfpx_status moe_layer_forward(const moe_layer *L, const void *x_dev, int xtype,
                               int q, float *y_dev, void *ws_dev,
                               size_t ws_bytes, void *stream);
 
-/* moe_layer_forward that also records caller-created hipEvent_t handles on
- * `stream`: events[0] before the router kernel, events[1] after it,
- * events[2] after the gate/up kernel, events[3] after the down kernel,
- * events[4] after the combine kernel.  For measuring each kernel of a step
- * inside a timed loop; events may be NULL (then it is moe_layer_forward).
- * The events must belong to the current device. */
+/* moe_layer_forward that also records four caller-created hipEvent_t
+ * handles on `stream`: events[0] before the first kernel (router scores and
+ * prepared activations), events[1] after it, events[2] after the gate/up
+ * kernel, events[3] after the down-and-combine kernel.  For measuring each
+ * kernel of a step inside a timed loop; events may be NULL (then it is
+ * moe_layer_forward).  The events must belong to the current device. */
 rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x_dev,
                                     int xtype, int q, float *y_dev,
                                     void *ws_dev, size_t ws_bytes,
