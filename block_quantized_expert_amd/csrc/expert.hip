@@ -160,12 +160,16 @@ __device__ __forceinline__ void unit_compute(const uint32_t (&cw)[R][NM][Fmt<FMT
         const float s = block_scale<FMT>(block_scale_bits<FMT>(sw[i][m], j));
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          float acc = ncr[g][j];
+          // two accumulators halve the chain of dependent dot2 ops
+          float acc0 = ncr[g][j], acc1 = 0.f;
 #pragma unroll
           for (int v = 0; v < VX; ++v)
 #pragma unroll
-            for (int p = 0; p < 16; ++p) acc = dot2(pr[p], xr[g][j][v][p], acc);
-          tot[i][m][g] = fmaf(acc, s, tot[i][m][g]);
+            for (int p = 0; p < 16; p += 2) {
+              acc0 = dot2(pr[p], xr[g][j][v][p], acc0);
+              acc1 = dot2(pr[p + 1], xr[g][j][v][p + 1], acc1);
+            }
+          tot[i][m][g] = fmaf(acc0 + acc1, s, tot[i][m][g]);
         }
       }
     }
@@ -267,6 +271,98 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
   return v;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// One halving step of a multi-value reduction: lanes paired by the DPP
+// involution CTRL (which flips lane bit B, and maybe lower bits that no
+// earlier step has used) split each pair of values between them: the lane
+// with bit B clear keeps the even value plus its partner's even value, the
+// other the odd one.
+template <int CTRL, int B, int N>
+__device__ __forceinline__ void ms_step(const float (&v)[N], float (&w)[N / 2], int lane) {
+  const bool odd = (lane >> B) & 1;
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float keep = odd ? v[2 * i + 1] : v[2 * i];
+    const float send = odd ? v[2 * i] : v[2 * i + 1];
+    w[i] = keep + dpp_f<CTRL>(send);
+  }
+}
+
+// Sums of N values (N = 2, 4, 8, 16) over the 64 lanes of a wave, all at
+// once: log2(N) halving steps over lane bits 3, 2, 1, 0 (row_mirror,
+// row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2], in that order,
+// so that each step's partner agrees on every bit used before), plain DPP
+// sums over the remaining bits of a 16-lane row, and lane shuffles across
+// the four rows.  Lane l then holds the total of value ms_index<N>(l); the
+// lanes ms_writer<N>(l) hold each value once.  About 3N + 8 VALU ops
+// instead of 14 per value.
+template <int N>
+__device__ __forceinline__ float multi_sum(const float (&v)[N], int lane) {
+  float r;
+  if constexpr (N == 1) {
+    r = v[0];
+    r += dpp_f<0x140>(r);
+    r += dpp_f<0x141>(r);
+    r += dpp_f<0x4E>(r);
+    r += dpp_f<0xB1>(r);
+  } else {
+    float a[N / 2];
+    ms_step<0x140, 3, N>(v, a, lane);
+    if constexpr (N == 2) {
+      r = a[0];
+      r += dpp_f<0x141>(r);
+      r += dpp_f<0x4E>(r);
+      r += dpp_f<0xB1>(r);
+    } else {
+      float b[N / 4];
+      ms_step<0x141, 2, N / 2>(a, b, lane);
+      if constexpr (N == 4) {
+        r = b[0];
+        r += dpp_f<0x4E>(r);
+        r += dpp_f<0xB1>(r);
+      } else {
+        float c[N / 8];
+        ms_step<0x4E, 1, N / 4>(b, c, lane);
+        if constexpr (N == 8) {
+          r = c[0] + dpp_f<0xB1>(c[0]);
+        } else {
+          static_assert(N == 16, "multi_sum: N must be 1, 2, 4, 8 or 16");
+          float d[1];
+          ms_step<0xB1, 0, 2>(c, d, lane);
+          r = d[0];
+        }
+      }
+    }
+  }
+  r += __shfl_xor(r, 16, 64);
+  r += __shfl_xor(r, 32, 64);
+  return r;
+}
+
+template <int N>
+__device__ __forceinline__ int ms_index(int lane) {
+  const int b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1, b0 = lane & 1;
+  if (N == 1) return 0;
+  if (N == 2) return b3;
+  if (N == 4) return b3 + 2 * b2;
+  if (N == 8) return b3 + 2 * b2 + 4 * b1;
+  return b3 + 2 * b2 + 4 * b1 + 8 * b0;
+}
+
+template <int N>
+__device__ __forceinline__ bool ms_writer(int lane) {
+  if (lane >= 16) return false;
+  if (N == 1) return lane == 0;
+  if (N == 2) return (lane & 7) == 0;
+  if (N == 4) return (lane & 3) == 0;
+  if (N == 8) return (lane & 1) == 0;
+  return true;
+}
+
 // Where a unit lies: unit u covers rows [rloc_u, rloc_u + R*rpi) of the tile
 // (rows rloc_u + rg + rpi*i for the lane's row group rg) and column part
 // u % parts (chunks 64p .. 64p+63 of each row when a row has 128 chunks).
@@ -316,16 +412,33 @@ __device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc
   while (true) {
     float tot[R][2][GP];
     unit_compute<FMT, GP, VX, 2, R>(cw, sw, xr, ncr, one, tot);
+    if (geo.lpr == 64) {  // one row per wave step: reduce all values at once
+      constexpr int N = R * 2 * GP;
+      float flat[N];
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+      for (int i = 0; i < R; ++i)
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-          const float v = group_sum(tot[i][m][g], geo.lpr);
-          if (li == 0)
-            gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i] = v;
-        }
+          for (int g = 0; g < GP; ++g) flat[(i * 2 + m) * GP + g] = tot[i][m][g];
+      const float v = multi_sum<N>(flat, lane);
+      if (ms_writer<N>(lane)) {
+        const int n = ms_index<N>(lane);
+        const int i = n / (2 * GP), m = (n / GP) % 2, g = n % GP;
+        gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + i] = v;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int g = 0; g < GP; ++g) {
+            const float v = group_sum(tot[i][m][g], geo.lpr);
+            if (li == 0)
+              gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i] = v;
+          }
+    }
     u += waves;
     if (u >= units) break;
     up = unit_pos(u, P, R, geo.rpi);
@@ -488,15 +601,36 @@ __device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, 
   float to[R][1][GP];
   unit_compute<FMT, GP, 2, 1, R>(cw, sw, xr, ncr, one_one_vgpr(), to);
   const int rw = a.rw_dn;
+  int col[GP];
+  float wgt[GP];
 #pragma unroll
   for (int g = 0; g < GP; ++g) {
-    const int col = sc.col(c0 + g);
-    const float wA = sc.weight(c0 + g);
+    col[g] = sc.col(c0 + g);
+    wgt[g] = sc.weight(c0 + g);
+  }
+  if (geo.lpr == 64) {  // one row per wave step: reduce all values at once
+    constexpr int N = R * GP;
+    float flat[N];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const float v = group_sum(to[i][0][g], geo.lpr);
-      if (li == 0) accw[col * rw + up.rloc_u + rg + geo.rpi * i] += wA * v;
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int g = 0; g < GP; ++g) flat[i * GP + g] = to[i][0][g];
+    const float v = multi_sum<N>(flat, lane);
+    if (ms_writer<N>(lane)) {
+      const int n = ms_index<N>(lane);
+      const int i = n / GP, g = n % GP;
+      const int cg = (GP == 2 && g) ? col[GP - 1] : col[0];
+      const float wg = (GP == 2 && g) ? wgt[GP - 1] : wgt[0];
+      accw[cg * rw + up.rloc_u + i] += wg * v;
     }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float v = group_sum(to[i][0][g], geo.lpr);
+        if (li == 0) accw[col[g] * rw + up.rloc_u + rg + geo.rpi * i] += wgt[g] * v;
+      }
   }
 }
 

@@ -136,54 +136,93 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return dpp_max(dpp_max(r0, r1), dpp_max(r2, r3));
 }
 
-// k rounds of a wave-wide arg-max over (score descending, index ascending)
-// for column c; lane l holds experts l, l+64, ...  Each round: every lane
-// offers its best untaken expert, the wave maximum of the keys is found
-// with DPP, and among the lanes offering it the lowest expert index wins
-// (one lane in all but exact ties).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Sorted top-k of column c and its gating weights, by one wave; lane l
+// holds experts l, l+64, ... (P of them, E <= 64 P).  Each lane first sorts
+// its own keys (score descending, index ascending: a compare-exchange
+// network on static indices), so that every round only looks at the lanes'
+// heads: the wave maximum of the heads (DPP), the lowest expert index among
+// the lanes holding it (one lane in all but exact ties), and that lane
+// drops its head.  Lane r < k keeps the r-th expert and score; the softmax
+// over the k scores is lane-parallel.  Writes s_ids[0..k) and s_w[0..k).
+template <int P>
 __device__ __forceinline__ void topk_wave(const RouteParams &rp, int c, int lane,
-                                          int32_t *ids, float *vals) {
-  constexpr int PER = kEMax / 64;
-  uint32_t key[PER];
-  float sv[PER];
+                                          int32_t *s_ids, float *s_w) {
+  uint32_t key[P];
+  int idx[P];
+  float sv[P];
   // unconditional loads (clamped index) so that all of them are in flight
   // together; entries past E get the key 0, below every real key
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
+  for (int i = 0; i < P; ++i) {
     const int e = lane + 64 * i;
     sv[i] = rp.scores[(size_t)c * rp.E + (e < rp.E ? e : rp.E - 1)];
   }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) key[i] = (lane + 64 * i < rp.E) ? score_key(sv[i]) : 0u;
-  for (int r = 0; r < rp.k; ++r) {
-    uint32_t kb = 0u;
-    int ib = 0x7FFFFFFF;
+  for (int i = 0; i < P; ++i) {
+    idx[i] = lane + 64 * i;
+    key[i] = idx[i] < rp.E ? score_key(sv[i]) : 0u;
+  }
+  // insertion network: after it key[0] >= key[1] >= ...; equal keys keep
+  // their index order (the swap is strict)
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (64 * i >= rp.E) break;
-      if (key[i] > kb) {  // strict: the lower i (lower index) keeps a tie
-        kb = key[i];
-        ib = lane + 64 * i;
-      }
+  for (int i = 1; i < P; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j) {
+      const bool sw = key[j] > key[j - 1];
+      const uint32_t ka = key[j - 1], kb = key[j];
+      const int ia = idx[j - 1], ib = idx[j];
+      key[j - 1] = sw ? kb : ka;
+      key[j] = sw ? ka : kb;
+      idx[j - 1] = sw ? ib : ia;
+      idx[j] = sw ? ia : ib;
     }
-    const uint32_t kmax = wave_max_u32(kb);
-    const uint64_t cand = __ballot(kb == kmax);
-    int best = __builtin_amdgcn_readlane(ib, (int)__builtin_ctzll(cand));
+  int my_id = 0;
+  float my_val = 0.f;
+  for (int r = 0; r < rp.k; ++r) {
+    const uint32_t kmax = wave_max_u32(key[0]);
+    const uint64_t cand = __ballot(key[0] == kmax);
+    int best = __builtin_amdgcn_readlane(idx[0], (int)__builtin_ctzll(cand));
     if (cand & (cand - 1ull)) {  // exact tie between lanes: lowest index
       uint64_t m = cand;
       while (m) {
-        const int l = (int)__builtin_ctzll(m);
-        const int v = __builtin_amdgcn_readlane(ib, l);
+        const int v = __builtin_amdgcn_readlane(idx[0], (int)__builtin_ctzll(m));
         best = v < best ? v : best;
         m &= m - 1ull;
       }
     }
+    if (lane == (best & 63)) {  // the winner drops its head
 #pragma unroll
-    for (int i = 0; i < PER; ++i)  // taken (static indices: no scratch)
-      if (best == lane + 64 * i) key[i] = 0u;
+      for (int i = 0; i + 1 < P; ++i) {
+        key[i] = key[i + 1];
+        idx[i] = idx[i + 1];
+      }
+      key[P - 1] = 0u;
+    }
     const uint32_t u = (kmax & 0x80000000u) ? (kmax & 0x7FFFFFFFu) : ~kmax;
-    ids[r] = best;
-    vals[r] = __uint_as_float(u);
+    if (lane == r) {
+      my_id = best;
+      my_val = __uint_as_float(u);
+    }
+  }
+  // softmax over the k chosen scores, relative to the largest (lane 0)
+  const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
+  const float e = lane < rp.k ? expf(my_val - v0) : 0.f;
+  const float z = wave_sum_dpp(e);
+  if (lane < rp.k) {
+    s_ids[lane] = my_id;
+    s_w[lane] = e / z * rp.routed_scale;
   }
 }
 
@@ -192,17 +231,12 @@ __device__ __forceinline__ void topk_wave(const RouteParams &rp, int c, int lane
 __device__ __forceinline__ void route_wg(const RouteParams &rp, RouteLds *s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave < rp.q) {
-    int32_t ids[kKMax];
-    float vals[kKMax];
-    topk_wave(rp, wave, lane, ids, vals);
-    if (lane == 0) {
-      float z = 0.f;
-      for (int j = 0; j < rp.k; ++j) z += expf(vals[j] - vals[0]);
-      for (int j = 0; j < rp.k; ++j) {
-        s->ids[wave][j] = ids[j];
-        s->gw[wave][j] = expf(vals[j] - vals[0]) / z * rp.routed_scale;
-      }
-    }
+    const int E = rp.E;
+    if (E <= 64) topk_wave<1>(rp, wave, lane, s->ids[wave], s->gw[wave]);
+    else if (E <= 128) topk_wave<2>(rp, wave, lane, s->ids[wave], s->gw[wave]);
+    else if (E <= 256) topk_wave<4>(rp, wave, lane, s->ids[wave], s->gw[wave]);
+    else if (E <= 512) topk_wave<8>(rp, wave, lane, s->ids[wave], s->gw[wave]);
+    else topk_wave<16>(rp, wave, lane, s->ids[wave], s->gw[wave]);
   }
   __syncthreads();
   if (wave == 0) {
