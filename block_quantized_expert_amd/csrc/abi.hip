@@ -207,7 +207,10 @@ const char *rfpx_last_error(void) { return g_err; }
 
 size_t moe_workspace_bytes(const moe_layer *L, int q_or_T, int prefill) {
   ForwardPlan p;
-  if (prefill) return 0;  // the prefill path sizes its own workspace (prefill.hip)
+  if (prefill) {
+    if (check_layer(L)) return 0;
+    return prefill_layout(L, q_or_T, RFPX_X_F32, nullptr);  // fp32 x needs the most
+  }
   if (make_plan(L, q_or_T, RFPX_X_F32, &p)) return 0;  // fp32 x needs the most
   return p.wl.total;
 }
@@ -254,6 +257,32 @@ rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x, int xtype
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], p.stream);
   if (e == hipSuccess) e = launch_experts(p);
   return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_layer_forward: %s", hipGetErrorString(e));
+}
+
+rfpx_status moe_prefill_forward(const moe_layer *L, const void *x, int xtype, int T,
+                                float *y, void *ws, size_t ws_bytes, void *stream) {
+  rfpx_status st = check_layer(L);
+  if (st) return st;
+  if (xtype != RFPX_X_F32 && xtype != RFPX_X_BF16) return fail(RFPX_E_ARG, "xtype=%d", xtype);
+  if (T < 1 || T > 65536) return fail(RFPX_E_SHAPE, "T=%d: must be in [1, 65536]", T);
+  if (L->d % 64 || L->f % 64)
+    return fail(RFPX_E_SHAPE, "prefill needs d and f multiples of 64 (d=%d, f=%d)", L->d, L->f);
+  const size_t need = prefill_layout(L, T, xtype, nullptr);
+  if (!need) return fail(RFPX_E_SHAPE, "prefill: unsupported shape (T=%d)", T);
+  if (!L->router_w || !L->image) return fail(RFPX_E_ARG, "layer router or image is null");
+  if (!x || !y || !ws) return fail(RFPX_E_ARG, "x, y or workspace is null");
+  if ((uintptr_t)ws % 256) return fail(RFPX_E_ALIGN, "workspace not 256-byte aligned");
+  if ((uintptr_t)L->image % 256) return fail(RFPX_E_ALIGN, "image not 256-byte aligned");
+  if ((uintptr_t)L->router_w % 16 || (uintptr_t)x % 16)
+    return fail(RFPX_E_ALIGN, "router weights and x must be 16-byte aligned");
+  if (ws_bytes < need)
+    return fail(RFPX_E_WORKSPACE, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
+  const size_t image_bytes = image_layout(L->d, L->f, L->n_experts, L->fmts, nullptr);
+  if (image_bytes > 0xFFFFFFFFull)
+    return fail(RFPX_E_SHAPE, "prefill: image of %zu bytes exceeds 4 GiB", image_bytes);
+  hipError_t e = launch_prefill(L, x, xtype, T, y, static_cast<uint8_t *>(ws), image_bytes,
+                                (hipStream_t)stream);
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_prefill_forward: %s", hipGetErrorString(e));
 }
 
 }  // extern "C"

@@ -492,23 +492,6 @@ __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc
   }
 }
 
-// One pair word (hi and lo parts) of one block of h for the down format,
-// and its share of the block's accumulator start.
-template <int FMT_DN>
-__device__ __forceinline__ float prep_h_pair(const float *hblk, int p, uint32_t *dst) {
-  int lo, hi, klo, khi;
-  pair_def<FMT_DN>(p, lo, hi, klo, khi);
-  const float vl = hblk[lo], vh = hblk[hi];
-  const float lh = bf16_bits_to_float(float_to_bf16_rne(vl));
-  const float hh = bf16_bits_to_float(float_to_bf16_rne(vh));
-  const float ll = bf16_bits_to_float(float_to_bf16_rne(vl - lh));
-  const float hl = bf16_bits_to_float(float_to_bf16_rne(vh - hh));
-  float nc = 0.f;
-  dst[p] = prepared_pair<FMT_DN>(lh, hh, klo, khi, &nc);
-  dst[16 + p] = prepared_pair<FMT_DN>(ll, hl, klo, khi, &nc);
-  return nc;
-}
-
 // Gate/up tile `tile` of slot `slot`, then h of the tile prepared for the
 // slot's down matrix: 16 threads per (column, block), one pair word each;
 // the block's accumulator start is the sum of the 16 shares (aligned groups
@@ -536,9 +519,7 @@ __device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, 
       item = ((size_t)slot * a.q + ci) * a.nb_f + tile * nbt + bt;
       const float *hblk = hs + ci * a.rw_gu + 32 * bt;
       uint32_t *dst = a.hp + item * 32;
-      if (fdn == RFPX_FP2) share = prep_h_pair<RFPX_FP2>(hblk, p, dst);
-      else if (fdn == RFPX_FP3) share = prep_h_pair<RFPX_FP3>(hblk, p, dst);
-      else share = prep_h_pair<RFPX_FP4>(hblk, p, dst);
+      share = prep_h_pair_rt(fdn, hblk, p, dst);
     }
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);

@@ -1,16 +1,752 @@
-// prefill.hip -- prefill chunk through one layer (tokens grouped per expert,
-// grouped products on the matrix cores).  Page "DeepSeek V4 Flash 在 128GB
-// 锐龙 AI MAX+ 上跑到 32 tok/s" (taozi.news), section "稀疏预填充：约 250
-// tok/s": prefill is batched per layer.
-#include "rfpx_impl.hpp"
+// prefill.hip -- a prefill chunk of T tokens through one routed-MoE layer:
+// tokens grouped by expert, each expert's gate/up and down products as
+// dense tiles on the matrix cores (v_mfma_f32_16x16x32_bf16).
+//
+// Page "DeepSeek V4 Flash 在 128GB 锐龙 AI MAX+ 上跑到 32 tok/s" (taozi.news),
+// section "稀疏预填充": prefill is batched per layer; section "ROCmFPX":
+// gate/up FP2, down FP3, the shared expert FP4.  Page "Lucebox专攻DeepSeek
+// V4…" (m.mzlw.cn), section "MoE 专家并行": 256 routed experts, top-6, one
+// shared expert.
+//
+// The per-token result is the decode path's (moe_layer_forward with one
+// column per token); only the order of fp32 sums differs.  Launches:
+//   k_pf_scores  router scores S = X Wr^T, fp32 tiles through LDS.
+//   k_pf_prep    prepared activations of every token and block for each
+//                gate/up format present (the decode path's pair words and
+//                accumulator starts, rfpx_impl.hpp).
+//   k_pf_topk    sorted top-k and gating weights, one wave per token.
+//   k_pf_group   one workgroup per expert: the (token, rank, weight) entries
+//                that chose it, in token order (stable); the shared expert
+//                takes every token at rank k with weight 1.
+//   k_pf_plan    row offsets of each expert's rows of h, and the task list:
+//                (expert, first row, rows) chunks of at most 128 rows, full
+//                chunks first, then the rest by size (largest first).
+//   k_pf_gateup  grid (f/64, tasks): a task's tokens x 64 rows of gate and
+//                up.  Each wave owns 16 rows and every 16-token tile of the
+//                task.  Per 32-weight block the B operand is the block's
+//                decoded pair words (the same v_and_or decode as the decode
+//                path; four per lane), the A operand the prepared
+//                activations and the C operand the block's accumulator start,
+//                so the MFMA result is sum_j (c_j - o) x_j exactly up to fp32
+//                rounding; the block scale is applied in fp32 to that
+//                result.  h = silu(g) * u, then prepared (bf16 hi + lo pair
+//                words for the expert's down format) as rows of hp.
+//   k_pf_down    grid (d/64, tasks): the down product of the task's rows of
+//                h (two MFMAs per block, hi and lo), times the gating
+//                weight, into out[token][rank][d].
+//   k_pf_combine y[t] = sum over ranks 0..k (the shared expert last).
+#include <type_traits>
 
-using namespace rfpx;
+#include "rfpx_route.hpp"
 
-extern "C" rfpx_status moe_prefill_forward(const moe_layer *L, const void *x,
-                                           int xtype, int T, float *y,
-                                           void *ws, size_t ws_bytes,
-                                           void *stream) {
-  (void)L; (void)x; (void)xtype; (void)T; (void)y; (void)ws; (void)ws_bytes;
-  (void)stream;
-  return fail(RFPX_E_SHAPE, "moe_prefill_forward: not available in this build");
+namespace rfpx {
+namespace {
+
+constexpr int kChunk = 128;   // rows (tokens) per task
+constexpr int kTileN = 64;    // output rows per workgroup: 4 waves x 16
+constexpr int kMT = kChunk / 16;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+struct PfTask {
+  int expert, m0, rows, pad;
+};
+
+struct PfArgs {
+  const uint8_t *image;
+  size_t image_bytes;
+  const float *wr;
+  const void *x;
+  float *y;
+  int d, f, E, k, T, xtype, vx, nb_d, nb_f;
+  float routed_scale;
+  int rows_max, max_tasks;
+  unsigned gu_fmts;
+  int fmt_slot[5];
+  // workspace
+  float *scores;       // [T][E]
+  int32_t *ids;        // [T][k]
+  float *gw;           // [T][k]
+  int32_t *counts;     // [E+1]
+  int32_t *ltok;       // [E+1][T]
+  int32_t *lrank;      // [E+1][T]
+  float *lw;           // [E+1][T]
+  int32_t *offs;       // [E+2]
+  int32_t *ntasks;     // [1]
+  PfTask *tasks;       // [max_tasks]
+  uint32_t *xp;        // [fmt slot][T][nb_d][vx][16]
+  float *xnc;          // [fmt slot][nb_d][T]
+  uint32_t *hp;        // [rows_max + 16][nb_f][32]
+  float *hnc;          // [nb_f][rows_max + 16]
+  float *out;          // [T][k+1][d]
+};
+
+__device__ __forceinline__ float load_x(const PfArgs &a, int t, int i) {
+  if (a.xtype == RFPX_X_BF16)
+    return bf16_bits_to_float(static_cast<const uint16_t *>(a.x)[(size_t)t * a.d + i]);
+  return static_cast<const float *>(a.x)[(size_t)t * a.d + i];
 }
+
+// ---------------------------------------------------------------- scores
+
+// S[t][e] = sum_i x[t][i] Wr[e][i]: 64 x 64 output tiles, k in steps of 32
+// through LDS, 4 x 4 outputs per thread, fp32 FMA.
+__global__ __launch_bounds__(256) void k_pf_scores(PfArgs a) {
+  __shared__ float xs[32][65];
+  __shared__ float ws[32][65];
+  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = 0; k0 < a.d; k0 += 32) {
+    for (int i = tid; i < 64 * 32; i += 256) {
+      const int r = i >> 5, c = i & 31;
+      const int t = t0 + r, e = e0 + r;
+      xs[c][r] = t < a.T ? load_x(a, t, k0 + c) : 0.f;
+      ws[c][r] = e < a.E ? a.wr[(size_t)e * a.d + k0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      float xv[4], wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[i] = xs[kk][ty * 4 + i];
+        wv[i] = ws[kk][tx * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
+      if (t < a.T && e < a.E) a.scores[(size_t)t * a.E + e] = acc[i][j];
+    }
+}
+
+// ------------------------------------------------- prepared activations
+
+template <int FMT>
+__device__ void pf_prep_item(const PfArgs &a, int slot, int t, int b) {
+  uint32_t hi[32], lo[32], pw[16];
+  float nc_hi, nc_lo = 0.f;
+  if (a.xtype == RFPX_X_BF16) {
+    const uint16_t *xs = static_cast<const uint16_t *>(a.x) + (size_t)t * a.d + 32 * b;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) hi[j] = xs[j];
+  } else {
+    const float *xs = static_cast<const float *>(a.x) + (size_t)t * a.d + 32 * b;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float v = xs[j];
+      hi[j] = float_to_bf16_rne(v);
+      lo[j] = float_to_bf16_rne(v - bf16_bits_to_float(hi[j]));
+    }
+  }
+  uint32_t *dst = a.xp + (((size_t)slot * a.T + t) * a.nb_d + b) * a.vx * 16;
+  prep_pairs<FMT>(hi, pw, &nc_hi);
+#pragma unroll
+  for (int p = 0; p < 16; ++p) dst[p] = pw[p];
+  if (a.vx == 2) {
+    prep_pairs<FMT>(lo, pw, &nc_lo);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) dst[16 + p] = pw[p];
+  }
+  a.xnc[((size_t)slot * a.nb_d + b) * a.T + t] = nc_hi + nc_lo;
+}
+
+__global__ __launch_bounds__(256) void k_pf_prep(PfArgs a) {
+  const int item = blockIdx.x * 256 + threadIdx.x;
+  const int per_fmt = a.T * a.nb_d;
+  const int nf = __builtin_popcount(a.gu_fmts);
+  if (item >= nf * per_fmt) return;
+  const int slot = item / per_fmt, rem = item % per_fmt;
+  const int t = rem / a.nb_d, b = rem % a.nb_d;
+  int fmt = 0;
+  for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
+    if (((a.gu_fmts >> f) & 1u) && a.fmt_slot[f] == slot) fmt = f;
+  if (fmt == RFPX_FP2) pf_prep_item<RFPX_FP2>(a, slot, t, b);
+  else if (fmt == RFPX_FP3) pf_prep_item<RFPX_FP3>(a, slot, t, b);
+  else if (fmt == RFPX_FP4) pf_prep_item<RFPX_FP4>(a, slot, t, b);
+}
+
+// ----------------------------------------------------------------- top-k
+
+__global__ __launch_bounds__(512) void k_pf_topk(PfArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 8 + wave;
+  if (t >= a.T) return;
+  RouteParams rp;
+  rp.scores = a.scores;
+  rp.E = a.E;
+  rp.k = a.k;
+  rp.q = 1;
+  rp.routed_scale = a.routed_scale;
+  int32_t *ids = a.ids + (size_t)t * a.k;
+  float *w = a.gw + (size_t)t * a.k;
+  if (a.E <= 64) topk_wave<1>(rp, t, lane, ids, w);
+  else if (a.E <= 128) topk_wave<2>(rp, t, lane, ids, w);
+  else if (a.E <= 256) topk_wave<4>(rp, t, lane, ids, w);
+  else if (a.E <= 512) topk_wave<8>(rp, t, lane, ids, w);
+  else topk_wave<16>(rp, t, lane, ids, w);
+}
+
+// -------------------------------------------------------------- grouping
+
+// Entries (token, rank, weight) of expert blockIdx.x in token order: chunks
+// of 256 (token, rank) entries, compacted with a ballot per wave and the
+// wave counts through LDS.
+__global__ __launch_bounds__(256) void k_pf_group(PfArgs a) {
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t *ltok = a.ltok + (size_t)e * a.T;
+  int32_t *lrank = a.lrank + (size_t)e * a.T;
+  float *lw = a.lw + (size_t)e * a.T;
+  if (e == a.E) {  // the shared expert: every token, rank k, weight 1
+    for (int t = tid; t < a.T; t += 256) {
+      ltok[t] = t;
+      lrank[t] = a.k;
+      lw[t] = 1.f;
+    }
+    if (tid == 0) a.counts[e] = a.T;
+    return;
+  }
+  __shared__ int wcount[4];
+  int base = 0;
+  const int n = a.T * a.k;
+  for (int j0 = 0; j0 < n; j0 += 256) {
+    const int j = j0 + tid;
+    const bool hit = j < n && a.ids[j] == e;
+    const uint64_t m = __ballot(hit);
+    const int before = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int woff = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) woff += wcount[w];
+      total += wcount[w];
+    }
+    if (hit) {
+      const int pos = base + woff + before;
+      ltok[pos] = j / a.k;
+      lrank[pos] = j % a.k;
+      lw[pos] = a.gw[j];
+    }
+    base += total;
+    __syncthreads();
+  }
+  if (tid == 0) a.counts[e] = base;
+}
+
+// Row offsets (exclusive scan of the counts) and the task list.  One
+// workgroup of 1024 threads; experts e = tid, tid + 1024.
+__global__ __launch_bounds__(1024) void k_pf_plan(PfArgs a) {
+  __shared__ int cnt[1025], scan[1025], rem_rank_base[1];
+  const int tid = threadIdx.x, ne = a.E + 1;
+  for (int e = tid; e < ne; e += 1024) cnt[e] = a.counts[e];
+  __syncthreads();
+  if (tid == 0) {
+    // exclusive scans of rows and of full chunks (serial: at most 1025)
+    int rows = 0, full = 0;
+    for (int e = 0; e < ne; ++e) {
+      scan[e] = full;
+      a.offs[e] = rows;
+      rows += cnt[e];
+      full += cnt[e] / kChunk;
+    }
+    a.offs[ne] = rows;
+    rem_rank_base[0] = full;
+  }
+  __syncthreads();
+  const int nfull = rem_rank_base[0];
+  int nrem = 0;
+  for (int e = 0; e < ne; ++e) nrem += (cnt[e] % kChunk) != 0;
+  for (int e = tid; e < ne; e += 1024) {
+    const int c = cnt[e], fc = c / kChunk, r = c % kChunk;
+    for (int i = 0; i < fc; ++i) {
+      PfTask t;
+      t.expert = e;
+      t.m0 = i * kChunk;
+      t.rows = kChunk;
+      t.pad = 0;
+      a.tasks[scan[e] + i] = t;
+    }
+    if (r) {
+      // rank among the remainder chunks: larger first, then lower expert
+      int rank = 0;
+      for (int e2 = 0; e2 < ne; ++e2) {
+        const int r2 = cnt[e2] % kChunk;
+        rank += r2 > r || (r2 == r && e2 < e);
+      }
+      PfTask t;
+      t.expert = e;
+      t.m0 = fc * kChunk;
+      t.rows = r;
+      t.pad = 0;
+      a.tasks[nfull + rank] = t;
+    }
+  }
+  if (tid == 0) a.ntasks[0] = nfull + nrem;
+}
+
+// ------------------------------------------------------ MFMA operands
+
+// Per-lane decode of pairs 4kq..4kq+3 of one block (the B operand of a
+// 16x16x32 MFMA: lane l holds k = 8(l/16) .. +7 of column l%16, i.e. pair
+// words 4kq .. 4kq+3 with kq = l/16).  The shifts and masks per lane put
+// each code at the mantissa position its pair has in the full-block decode
+// (decode_pairs), so the prepared activations match.
+template <int FMT>
+struct QuadDecode {
+  uint32_t sh[4], mk[4];
+  uint32_t bsh;  // FP3: first bit of the lane's 64-bit window
+  int word;      // code dword (FP2, FP4) or first dword - 1 (FP3) of the lane
+  __device__ void init(int kq) {
+    if (FMT == RFPX_FP2) {
+      const bool odd = kq & 1;
+      const uint32_t M0 = 0x00030003u, M1 = 0x000C000Cu, M2 = 0x00300030u;
+      sh[0] = odd ? 6 : 0;
+      sh[1] = odd ? 6 : 0;
+      sh[2] = odd ? 12 : 0;
+      sh[3] = odd ? 12 : 6;
+      mk[0] = odd ? M1 : M0;
+      mk[1] = odd ? M2 : M1;
+      mk[2] = odd ? M0 : M2;
+      mk[3] = odd ? M1 : M0;
+      word = kq >> 1;
+      bsh = 0;
+    } else if (FMT == RFPX_FP4) {
+      sh[0] = 0;
+      sh[1] = 1;
+      sh[2] = 5;
+      sh[3] = 9;
+      mk[0] = 0x000F000Fu;
+      mk[1] = mk[2] = mk[3] = 0x00780078u;
+      word = kq;
+      bsh = 0;
+    } else {
+      // the lane's 64-bit window starts at bit -4, 8, 35, 64 of the block's
+      // 96-bit code word (kq = 0..3); pairs 4kq..4kq+3 sit at these offsets
+      // into it (selects, not a table: a per-lane table index would go to
+      // scratch memory)
+      const uint32_t MA = 0x00380070u, MB = 0x0070001Cu;
+      sh[0] = 0;
+      sh[1] = kq == 1 ? 18 : 3;
+      sh[2] = kq == 1 ? 21 : kq == 2 ? 23 : 6;
+      sh[3] = kq == 1 ? 24 : kq == 2 ? 26 : 9;
+      mk[0] = kq == 3 ? MB : MA;
+      mk[1] = kq == 3 ? MB : MA;
+      mk[2] = kq >= 2 ? MB : MA;
+      mk[3] = kq >= 2 ? MB : MA;
+      word = kq - 1;
+      bsh = kq == 0 ? 28 : kq == 1 ? 8 : kq == 2 ? 3 : 0;
+    }
+  }
+};
+
+// Decoded pair words of one lane from its code dwords q (1 for FP2/FP4, 3
+// for FP3: the dwords at word-1 .. word+1 of the block).
+template <int FMT>
+__device__ __forceinline__ void decode_quad(const QuadDecode<FMT> &qd, const uint32_t *q,
+                                            uint32_t one, uint32_t *pw) {
+  if (FMT == RFPX_FP3) {
+    const uint32_t u0 = __builtin_amdgcn_alignbit(q[1], q[0], qd.bsh);
+    const uint32_t u1 = __builtin_amdgcn_alignbit(q[2], q[1], qd.bsh);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      pw[j] = and_or(__builtin_amdgcn_alignbit(u1, u0, qd.sh[j]), qd.mk[j], one);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pw[j] = and_or(q[0] >> qd.sh[j], qd.mk[j], one);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_quad(__amdgpu_buffer_rsrc_t r, uint32_t block_off,
+                                          const QuadDecode<FMT> &qd, uint32_t *q) {
+  if (FMT == RFPX_FP3) {
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, (int)(block_off + 4 * qd.word), 0, 0);
+    q[0] = v.x;
+    q[1] = v.y;
+    q[2] = v.z;
+  } else {
+    q[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)(block_off + 4 * qd.word), 0, 0);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ float load_block_scale(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if (FMT == RFPX_FP4) return block_scale<RFPX_FP4>(__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0));
+  return block_scale<FMT>(__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t *w) {
+  u32x4 v;
+  v.x = w[0];
+  v.y = w[1];
+  v.z = w[2];
+  v.w = w[3];
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ floatx4 mfma(const bf16x8 &a, const bf16x8 &b, const floatx4 &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------- gate / up
+
+template <int FMT, int VX>
+__device__ void pf_gateup_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed,
+                               float *hs /* [kChunk][64] */, float *ncs /* [2][kChunk] */,
+                               int *toks /* [kChunk] */) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kq = lane >> 4, col = lane & 15;
+  const int e = tk.expert, m0 = tk.m0, cnt = tk.rows;
+  const int nmt = (cnt + 15) >> 4;
+  const int slot = a.fmt_slot[FMT];
+  const int n0 = blockIdx.x * kTileN;
+  const int my_row = n0 + 16 * wave + col;
+  for (int r = tid; r < kChunk; r += 256) toks[r] = r < cnt ? a.ltok[(size_t)e * a.T + m0 + r] : 0;
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t img = make_rsrc(a.image, (uint32_t)a.image_bytes);
+  const __amdgpu_buffer_rsrc_t xpr =
+      make_rsrc(a.xp, (uint32_t)((size_t)__builtin_popcount(a.gu_fmts) * a.T * a.nb_d * a.vx * 64));
+  QuadDecode<FMT> qd;
+  qd.init(kq);
+  const uint32_t cb = code_bytes(FMT), sb = scale_bytes(FMT);
+  uint32_t coff[2], soff[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    coff[m] = (uint32_t)(ed.codes[m] + (size_t)my_row * a.nb_d * cb);
+    soff[m] = (uint32_t)(ed.scales[m] + (size_t)my_row * a.nb_d * sb);
+  }
+  int tokA[kMT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) tokA[mt] = toks[mt * 16 + col];
+  floatx4 acc[kMT][2];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) acc[mt][m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t one = one_one_vgpr();
+  const float *xnc = a.xnc + (size_t)slot * a.nb_d * a.T;
+  // accumulator starts of block 0
+  for (int r = tid; r < cnt; r += 256) ncs[r] = xnc[toks[r]];
+  __syncthreads();
+  for (int b = 0; b < a.nb_d; ++b) {
+    float *ncb = ncs + (b & 1) * kChunk;
+    if (b + 1 < a.nb_d) {
+      float *ncn = ncs + ((b + 1) & 1) * kChunk;
+      for (int r = tid; r < cnt; r += 256) ncn[r] = xnc[(size_t)(b + 1) * a.T + toks[r]];
+    }
+    bf16x8 bop[2];
+    float sc[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      uint32_t q[3], pw[4];
+      load_quad<FMT>(img, coff[m] + b * cb, qd, q);
+      sc[m] = load_block_scale<FMT>(img, soff[m] + b * sb);
+      decode_quad<FMT>(qd, q, one, pw);
+      bop[m] = as_bf16x8(pw);
+    }
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      if (mt < nmt) {
+        const uint32_t xoff =
+            (uint32_t)((((size_t)slot * a.T + tokA[mt]) * a.nb_d + b) * a.vx * 64 + 16 * kq);
+        const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(xpr, (int)xoff, 0, 0);
+        const floatx4 c = *reinterpret_cast<const floatx4 *>(ncb + mt * 16 + 4 * kq);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a0);
+        bf16x8 av1 = av;
+        if constexpr (VX == 2)
+          av1 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xpr, (int)(xoff + 64), 0, 0));
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          floatx4 p = mfma(av, bop[m], c);
+          if constexpr (VX == 2) p = mfma(av1, bop[m], p);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][m][i] = fmaf(sc[m], p[i], acc[mt][m][i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // h = silu(g) * u into LDS: rows m = 16 mt + 4 kq + i, column 16 wave + col
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+    if (mt < nmt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hs[(mt * 16 + 4 * kq + i) * kTileN + 16 * wave + col] = silu(acc[mt][0][i]) * acc[mt][1][i];
+  __syncthreads();
+  // prepare h for the down matrix: 16 threads per (row, f-block)
+  const int fdn = ed.fmt[2];
+  const int nfb = kTileN / 32;
+  const int nitems = cnt * nfb * 16;
+  const int rowbase = a.offs[e] + m0;
+  for (int base = 0; base < nitems; base += 256) {
+    const int it = base + tid;
+    float share = 0.f;
+    size_t hrow = 0;
+    int fbg = 0;
+    if (it < nitems) {
+      const int p = it & 15, rb = it >> 4;
+      const int r = rb / nfb, fb = rb % nfb;
+      fbg = n0 / 32 + fb;
+      hrow = (size_t)rowbase + r;
+      const float *hblk = hs + r * kTileN + 32 * fb;
+      uint32_t *dst = a.hp + (hrow * a.nb_f + fbg) * 32;
+      share = prep_h_pair_rt(fdn, hblk, p, dst);
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
+    if (it < nitems && (it & 15) == 0) a.hnc[(size_t)fbg * (a.rows_max + 16) + hrow] = share;
+  }
+}
+
+template <int VX>
+__global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
+  if ((int)blockIdx.y >= a.ntasks[0]) return;
+  const PfTask tk = a.tasks[blockIdx.y];
+  __shared__ __align__(16) float hs[kChunk * kTileN];
+  __shared__ __align__(16) float ncs[2 * kChunk];
+  __shared__ int toks[kChunk];
+  const ExpertDesc *tab = reinterpret_cast<const ExpertDesc *>(a.image + kImgTable);
+  ExpertDesc ed;
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    ed.codes[m] = uniform64(tab[tk.expert].codes[m]);
+    ed.scales[m] = uniform64(tab[tk.expert].scales[m]);
+    ed.fmt[m] = uniform(tab[tk.expert].fmt[m]);
+  }
+  const int fmt = ed.fmt[0];
+  if (fmt == RFPX_FP2) pf_gateup_task<RFPX_FP2, VX>(a, tk, ed, hs, ncs, toks);
+  else if (fmt == RFPX_FP3) pf_gateup_task<RFPX_FP3, VX>(a, tk, ed, hs, ncs, toks);
+  else pf_gateup_task<RFPX_FP4, VX>(a, tk, ed, hs, ncs, toks);
+}
+
+// ------------------------------------------------------------------- down
+
+template <int FMT>
+__device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kq = lane >> 4, col = lane & 15;
+  const int e = tk.expert, m0 = tk.m0, cnt = tk.rows;
+  const int nmt = (cnt + 15) >> 4;
+  const int n0 = blockIdx.x * kTileN;
+  const int my_row = n0 + 16 * wave + col;
+  const int rowbase = a.offs[e] + m0;
+  const __amdgpu_buffer_rsrc_t img = make_rsrc(a.image, (uint32_t)a.image_bytes);
+  const size_t hp_bytes = (size_t)(a.rows_max + 16) * a.nb_f * 128;
+  const __amdgpu_buffer_rsrc_t hpr = make_rsrc(a.hp, (uint32_t)hp_bytes);
+  const __amdgpu_buffer_rsrc_t hncr =
+      make_rsrc(a.hnc, (uint32_t)((size_t)a.nb_f * (a.rows_max + 16) * 4));
+  QuadDecode<FMT> qd;
+  qd.init(kq);
+  const uint32_t cb = code_bytes(FMT), sb = scale_bytes(FMT);
+  const uint32_t coff = (uint32_t)(ed.codes[2] + (size_t)my_row * a.nb_f * cb);
+  const uint32_t soff = (uint32_t)(ed.scales[2] + (size_t)my_row * a.nb_f * sb);
+  floatx4 acc[kMT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t one = one_one_vgpr();
+  for (int b = 0; b < a.nb_f; ++b) {
+    uint32_t q[3], pw[4];
+    load_quad<FMT>(img, coff + b * cb, qd, q);
+    const float sc = load_block_scale<FMT>(img, soff + b * sb);
+    decode_quad<FMT>(qd, q, one, pw);
+    const bf16x8 bop = as_bf16x8(pw);
+    const uint32_t hncb = (uint32_t)(((size_t)b * (a.rows_max + 16) + rowbase) * 4);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      if (mt < nmt) {
+        const uint32_t hoff =
+            (uint32_t)((((size_t)rowbase + mt * 16 + col) * a.nb_f + b) * 128 + 16 * kq);
+        const u32x4 ahi = __builtin_amdgcn_raw_buffer_load_b128(hpr, (int)hoff, 0, 0);
+        const u32x4 alo = __builtin_amdgcn_raw_buffer_load_b128(hpr, (int)(hoff + 64), 0, 0);
+        const floatx4 c = __builtin_bit_cast(
+            floatx4, __builtin_amdgcn_raw_buffer_load_b128(hncr, (int)(hncb + 4 * (mt * 16 + 4 * kq)), 0, 0));
+        floatx4 p = mfma(__builtin_bit_cast(bf16x8, ahi), bop, c);
+        p = mfma(__builtin_bit_cast(bf16x8, alo), bop, p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sc, p[i], acc[mt][i]);
+      }
+    }
+  }
+  const int *ltok = a.ltok + (size_t)e * a.T + m0;
+  const int *lrank = a.lrank + (size_t)e * a.T + m0;
+  const float *lw = a.lw + (size_t)e * a.T + m0;
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+    if (mt < nmt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = mt * 16 + 4 * kq + i;
+        if (r < cnt) {
+          const int t = ltok[r];
+          a.out[((size_t)t * (a.k + 1) + lrank[r]) * a.d + my_row] = lw[r] * acc[mt][i];
+        }
+      }
+}
+
+__global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
+  if ((int)blockIdx.y >= a.ntasks[0]) return;
+  const PfTask tk = a.tasks[blockIdx.y];
+  const ExpertDesc *tab = reinterpret_cast<const ExpertDesc *>(a.image + kImgTable);
+  ExpertDesc ed;
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    ed.codes[m] = uniform64(tab[tk.expert].codes[m]);
+    ed.scales[m] = uniform64(tab[tk.expert].scales[m]);
+    ed.fmt[m] = uniform(tab[tk.expert].fmt[m]);
+  }
+  const int fmt = ed.fmt[2];
+  if (fmt == RFPX_FP2) pf_down_task<RFPX_FP2>(a, tk, ed);
+  else if (fmt == RFPX_FP3) pf_down_task<RFPX_FP3>(a, tk, ed);
+  else pf_down_task<RFPX_FP4>(a, tk, ed);
+}
+
+// ---------------------------------------------------------------- combine
+
+__global__ __launch_bounds__(256) void k_pf_combine(PfArgs a) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (size_t)a.T * a.d) return;
+  const size_t t = i / a.d, n = i % a.d;
+  float v = 0.f;
+  for (int r = 0; r <= a.k; ++r) v += a.out[(t * (a.k + 1) + r) * a.d + n];
+  a.y[i] = v;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+// Workspace plan of the prefill path; returns 0 for an unsupported shape.
+size_t prefill_layout(const moe_layer *L, int T, int xtype, void *args_out) {
+  if (T < 1 || T > 65536) return 0;
+  PfArgs a{};
+  a.d = L->d;
+  a.f = L->f;
+  a.E = L->n_experts;
+  a.k = L->top_k;
+  a.T = T;
+  a.xtype = xtype;
+  a.vx = xtype == RFPX_X_BF16 ? 1 : 2;
+  a.nb_d = L->d / 32;
+  a.nb_f = L->f / 32;
+  a.routed_scale = L->routed_scale;
+  a.rows_max = T * (L->top_k + 1);
+  a.max_tasks = (L->n_experts + 1) + (a.rows_max + kChunk - 1) / kChunk;
+  int nf = 0;
+  for (int f = 0; f < 5; ++f) a.fmt_slot[f] = -1;
+  for (int e = 0; e <= L->n_experts; ++e) a.gu_fmts |= 1u << L->fmts[3 * e];
+  for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
+    if ((a.gu_fmts >> f) & 1u) a.fmt_slot[f] = nf++;
+  if (L->d % kTileN || L->f % kTileN) return 0;
+  const size_t E1 = L->n_experts + 1;
+  size_t off = 0;
+  struct Item {
+    size_t *dst;
+    size_t bytes;
+  };
+  size_t o_scores, o_ids, o_gw, o_counts, o_ltok, o_lrank, o_lw, o_offs, o_ntasks, o_tasks,
+      o_xp, o_xnc, o_hp, o_hnc, o_out;
+  const Item items[] = {
+      {&o_scores, (size_t)T * L->n_experts * 4},
+      {&o_ids, (size_t)T * L->top_k * 4},
+      {&o_gw, (size_t)T * L->top_k * 4},
+      {&o_counts, E1 * 4},
+      {&o_ltok, E1 * T * 4},
+      {&o_lrank, E1 * T * 4},
+      {&o_lw, E1 * T * 4},
+      {&o_offs, (E1 + 1) * 4},
+      {&o_ntasks, 4},
+      {&o_tasks, (size_t)a.max_tasks * sizeof(PfTask)},
+      {&o_xp, (size_t)nf * T * a.nb_d * a.vx * 64},
+      {&o_xnc, (size_t)nf * a.nb_d * T * 4},
+      {&o_hp, (size_t)(a.rows_max + 16) * a.nb_f * 128},
+      {&o_hnc, (size_t)a.nb_f * (a.rows_max + 16) * 4},
+      {&o_out, (size_t)T * (L->top_k + 1) * L->d * 4},
+  };
+  for (const Item &it : items) {
+    *it.dst = off;
+    off = align256(off + it.bytes);
+  }
+  // buffer resources address hp and xp with 32-bit offsets
+  if ((size_t)(a.rows_max + 16) * a.nb_f * 128 > 0xFFFFFFFFull) return 0;
+  if (args_out) {
+    a.scores = reinterpret_cast<float *>(o_scores);
+    a.ids = reinterpret_cast<int32_t *>(o_ids);
+    a.gw = reinterpret_cast<float *>(o_gw);
+    a.counts = reinterpret_cast<int32_t *>(o_counts);
+    a.ltok = reinterpret_cast<int32_t *>(o_ltok);
+    a.lrank = reinterpret_cast<int32_t *>(o_lrank);
+    a.lw = reinterpret_cast<float *>(o_lw);
+    a.offs = reinterpret_cast<int32_t *>(o_offs);
+    a.ntasks = reinterpret_cast<int32_t *>(o_ntasks);
+    a.tasks = reinterpret_cast<PfTask *>(o_tasks);
+    a.xp = reinterpret_cast<uint32_t *>(o_xp);
+    a.xnc = reinterpret_cast<float *>(o_xnc);
+    a.hp = reinterpret_cast<uint32_t *>(o_hp);
+    a.hnc = reinterpret_cast<float *>(o_hnc);
+    a.out = reinterpret_cast<float *>(o_out);
+    *static_cast<PfArgs *>(args_out) = a;
+  }
+  return off;
+}
+
+hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, float *y,
+                          uint8_t *ws, size_t image_bytes, hipStream_t stream) {
+  PfArgs a;
+  if (!prefill_layout(L, T, xtype, &a)) return hipErrorInvalidValue;
+  // turn workspace offsets into pointers
+  auto rel = [ws](auto *&p) { p = reinterpret_cast<std::remove_reference_t<decltype(p)>>(ws + reinterpret_cast<uintptr_t>(p)); };
+  rel(a.scores);
+  rel(a.ids);
+  rel(a.gw);
+  rel(a.counts);
+  rel(a.ltok);
+  rel(a.lrank);
+  rel(a.lw);
+  rel(a.offs);
+  rel(a.ntasks);
+  rel(a.tasks);
+  rel(a.xp);
+  rel(a.xnc);
+  rel(a.hp);
+  rel(a.hnc);
+  rel(a.out);
+  a.image = L->image;
+  a.image_bytes = image_bytes;
+  a.wr = L->router_w;
+  a.x = x;
+  a.y = y;
+  k_pf_scores<<<dim3((a.E + 63) / 64, (T + 63) / 64), 256, 0, stream>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nf = __builtin_popcount(a.gu_fmts);
+  const size_t nprep = (size_t)nf * T * a.nb_d;
+  k_pf_prep<<<(unsigned)((nprep + 255) / 256), 256, 0, stream>>>(a);
+  k_pf_topk<<<(T + 7) / 8, 512, 0, stream>>>(a);
+  k_pf_group<<<a.E + 1, 256, 0, stream>>>(a);
+  k_pf_plan<<<1, 1024, 0, stream>>>(a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 ggu(a.f / kTileN, a.max_tasks), gdn(a.d / kTileN, a.max_tasks);
+  if (a.vx == 1) k_pf_gateup<1><<<ggu, 256, 0, stream>>>(a);
+  else k_pf_gateup<2><<<ggu, 256, 0, stream>>>(a);
+  k_pf_down<<<gdn, 256, 0, stream>>>(a);
+  k_pf_combine<<<(unsigned)(((size_t)T * a.d + 255) / 256), 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace rfpx

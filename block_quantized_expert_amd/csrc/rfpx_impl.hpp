@@ -312,6 +312,47 @@ __device__ __forceinline__ void prep_pairs(const uint32_t *xb, uint32_t *pw, flo
   *nc = acc;
 }
 
+// One pair word of one block of h (fp32 values, split into bf16 hi + lo)
+// for a down matrix of format fmt (a runtime value): writes dst[p] (hi
+// parts) and dst[16 + p] (lo parts) and returns the pair's share of the
+// block's accumulator start.  A single code path for all formats: three
+// inlined template instances of this step behind a runtime format switch
+// have been merged by the compiler into one shared block whose FP4 exit lost
+// the address of the pair's second value.
+__device__ __forceinline__ float prep_h_pair_rt(int fmt, const float *hblk, int p,
+                                                uint32_t *dst) {
+  int lo, hi, klo, khi;
+  float o;
+  if (fmt == RFPX_FP2) {
+    const int i = p & 7;
+    lo = 16 * (p >> 3) + i;
+    hi = lo + 8;
+    klo = khi = 2 * (i % 3);
+    o = 1.5f;
+  } else if (fmt == RFPX_FP4) {
+    const int i = p & 3;
+    lo = 8 * (p >> 2) + i;
+    hi = lo + 4;
+    klo = khi = i == 0 ? 0 : 3;
+    o = 7.5f;
+  } else {
+    lo = p < 5 ? p : p < 10 ? p + 5 : 20 + (p - 10);
+    hi = p < 10 ? lo + 5 : lo + 6;
+    klo = p < 10 ? 4 : 2;
+    khi = p < 10 ? 3 : 4;
+    o = 3.5f;
+  }
+  const float vl = hblk[lo], vh = hblk[hi];
+  const float lh = bf16_bits_to_float(float_to_bf16_rne(vl));
+  const float hh = bf16_bits_to_float(float_to_bf16_rne(vh));
+  const float ll = bf16_bits_to_float(float_to_bf16_rne(vl - lh));
+  const float hl = bf16_bits_to_float(float_to_bf16_rne(vh - hh));
+  const float flo = (float)(1 << (7 - klo)), fhi = (float)(1 << (7 - khi));
+  dst[p] = (__float_as_uint(lh * flo) >> 16) | (__float_as_uint(hh * fhi) & 0xFFFF0000u);
+  dst[16 + p] = (__float_as_uint(ll * flo) >> 16) | (__float_as_uint(hl * fhi) & 0xFFFF0000u);
+  return -((flo + o) * (lh + ll) + (fhi + o) * (hh + hl));
+}
+
 // Block scale as an fp32 multiplier: fp16 bits (FP2/FP3) or E8M0 (FP4).
 template <int FMT>
 __device__ __forceinline__ float block_scale(uint32_t bits) {
@@ -379,6 +420,11 @@ struct ForwardPlan {
 // k_route: router scores and prepared activations; for route_only also
 // k_topk (ids and gating weights for moe_route_topk).
 hipError_t launch_route(const ForwardPlan &p);
+// Prefill (prefill.hip): workspace bytes for T tokens (0: unsupported
+// shape); with args_out, also the kernel arguments with workspace offsets.
+size_t prefill_layout(const moe_layer *L, int T, int xtype, void *args_out);
+hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, float *y,
+                          uint8_t *ws, size_t image_bytes, hipStream_t stream);
 // k_gateup (all slots) and k_down (all slots, with the combine); records
 // events[2] and events[3] when events are given.
 hipError_t launch_experts(const ForwardPlan &p);
