@@ -128,12 +128,86 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(args, cfg) -> int:
+    """The 2048-token prefill chunk: moe_prefill_forward over layer images
+    rotated so that no weight is re-read from the last-level cache."""
+    import numpy as np
+    import torch
+
+    import block_quantized_expert_amd as bqe
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bqe.lib()
+    n_layers = args.layers or 2
+    steps = min(args.steps, 40)
+    warm = min(args.warmup, 4)
+    layers = []
+    for l in range(n_layers):
+        lay = synth.gen_layer(cfg, l)
+        L = bqe.upload_layer(lay)
+        cols = synth.gen_columns(cfg, lay, cfg.q, layer=l)
+        x = torch.from_numpy(cols.x.view(np.int16)).view(torch.bfloat16).to(dev)
+        layers.append((L, x, bqe.workspace(L, cfg.q, prefill=True)))
+        weight_bytes = int(lay.blob.size)
+        del lay
+        print(f"# layer {l + 1}/{n_layers} ready", file=sys.stderr, flush=True)
+    y = torch.empty((cfg.q, cfg.d), dtype=torch.float32, device=dev)
+    for s in range(warm):
+        L, x, ws = layers[s % n_layers]
+        bqe.moe_prefill_forward(L, x, y=y, ws=ws)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(steps):
+        L, x, ws = layers[s % n_layers]
+        bqe.moe_prefill_forward(L, x, y=y, ws=ws)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    rows = cfg.q * (cfg.k + 1)
+    flops = 2.0 * rows * 3 * cfg.f * cfg.d  # gate, up and down of every (token, expert) row
+    out = {
+        "metric": "MoE-layer prefill tokens/s (2048-token chunk) and MFMA utilization",
+        "value": cfg.q / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "config_id": cfg.cid, "tokens": cfg.q, "d": cfg.d,
+                   "f": cfg.f, "experts": cfg.E, "top_k": cfg.k, "shared": 1,
+                   "formats": "gate/up FP2, down FP3, shared FP4", "activations": "bf16",
+                   "layers_rotated": n_layers, "seed_master": cfg.master},
+        "useful_gflop": flops / 1e9,
+        "mfma_utilization": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "roofline": {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                     "traffic": None, "kernel": "whole prefill chunk (all launches)"},
+        "weight_GB_per_s": weight_bytes / (ms * 1e-3) / 1e9,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4))
+    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
     ap.add_argument("--layers", type=int, default=0,
                     help="layer instances to rotate over (default 8; 43 for --config 4)")
     ap.add_argument("--variants", type=int, default=4,
@@ -156,6 +230,8 @@ def main() -> int:
     import synth
 
     cfg = synth.CONFIGS[args.config]
+    if cfg.prefill:
+        return bench_prefill(args, cfg)
     n_layers = args.layers or (43 if args.config == 4 else 8)
     q = cfg.q
     dev = torch.device("cuda:0")

@@ -42,8 +42,10 @@
 namespace rfpx {
 namespace {
 
-constexpr int kChunk = 128;   // rows (tokens) per task
-constexpr int kTileN = 64;    // output rows per workgroup: 4 waves x 16
+constexpr int kChunk = 64;      // rows (tokens) per task
+constexpr int kPfThreads = 512; // 8 waves per product workgroup
+constexpr int kTileGU = 256;    // gate/up rows per workgroup: 8 waves x 2 x 16
+constexpr int kTileDN = 512;    // down rows per workgroup: 8 waves x 4 x 16
 constexpr int kMT = kChunk / 16;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -405,184 +407,293 @@ __device__ __forceinline__ floatx4 mfma(const bf16x8 &a, const bf16x8 &b, const 
 
 // ------------------------------------------------------------- gate / up
 
+// Where each of a task's (at most kChunk) rows keeps its A operand and its
+// accumulator starts: byte offsets of block 0 (block b adds b times the
+// stride), and rows past the task's count alias a valid row.
+struct PfRows {
+  uint32_t a_row[kChunk];
+  uint32_t nc_row[kChunk];
+};
+
+// Output tile of a grouped product over nblocks blocks of 32: the task's
+// rows (at most kChunk) x NT 16-row tiles of NM matrices per wave, 8 waves
+// per workgroup.  Software-pipelined in chunks of KC blocks: while chunk c
+// is multiplied, the A words (and accumulator starts) of chunk c+1 are in
+// flight to registers, to be stored to the other LDS buffer, and the B code
+// words and scales of chunk c+1 to registers.  The A tile in LDS serves all
+// 8 x NT column tiles, so each A row is read from memory once per 128 NT
+// output rows.  NA = number of A terms per block (1, or 2 for bf16 hi +
+// lo), chained through the MFMA accumulator.
+template <int FMT, int NM, int NT, int NA, int KC>
+__device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
+                                        __amdgpu_buffer_rsrc_t ar, uint32_t a_stride,
+                                        __amdgpu_buffer_rsrc_t ncr, uint32_t nc_stride,
+                                        const PfRows &rows, const ExpertDesc &ed, int mat0,
+                                        int row0 /* first B row of this wave */, int nbB,
+                                        uint32_t *lds_a, float *lds_nc,
+                                        floatx4 (&acc)[kMT][NT][NM]) {
+  constexpr int AW = NA * 16, AWP = AW + 4, V4 = AW / 4;
+  constexpr int NLD = KC * kChunk * V4 / kPfThreads;
+  static_assert(NLD * kPfThreads == KC * kChunk * V4, "A loads must split evenly");
+  constexpr int QW = FMT == RFPX_FP3 ? 3 : 1;
+  const int tid = threadIdx.x, lane = tid & 63, kq = lane >> 4, col = lane & 15;
+  QuadDecode<FMT> qd;
+  qd.init(kq);
+  const __amdgpu_buffer_rsrc_t img = make_rsrc(a.image, (uint32_t)a.image_bytes);
+  const uint32_t cb = code_bytes(FMT), sb = scale_bytes(FMT);
+  uint32_t coff[NT][NM], soff[NT][NM];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const size_t row = (size_t)row0 + 16 * nt + col;
+      coff[nt][m] = (uint32_t)(ed.codes[mat0 + m] + row * nbB * cb);
+      soff[nt][m] = (uint32_t)(ed.scales[mat0 + m] + row * nbB * sb);
+    }
+  const int nchunks = (nblocks + KC - 1) / KC;
+  u32x4 ra[NLD];
+  float rnc = 0.f;
+  uint32_t bqn[NT][NM][KC][QW], bqc[NT][NM][KC][QW];
+  float bsn[NT][NM][KC], bsc[NT][NM][KC];
+  const uint32_t one = one_one_vgpr();
+
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int item = tid + kPfThreads * q;
+      const int r = item % kChunk, rest = item / kChunk;
+      const int j = rest / V4, w4 = rest % V4;
+      const int blk = min(c * KC + j, nblocks - 1);
+      ra[q] = __builtin_amdgcn_raw_buffer_load_b128(
+          ar, (int)(rows.a_row[r] + blk * a_stride + 16 * w4), 0, 0);
+    }
+    if (tid < KC * kChunk) {
+      const int r = tid % kChunk, j = tid / kChunk;
+      const int blk = min(c * KC + j, nblocks - 1);
+      rnc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                          ncr, (int)(rows.nc_row[r] + blk * nc_stride), 0, 0));
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+          const uint32_t blk = (uint32_t)min(c * KC + j, nblocks - 1);
+          load_quad<FMT>(img, coff[nt][m] + blk * cb, qd, bqn[nt][m][j]);
+          bsn[nt][m][j] = load_block_scale<FMT>(img, soff[nt][m] + blk * sb);
+        }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int item = tid + kPfThreads * q;
+      const int r = item % kChunk, rest = item / kChunk;
+      const int j = rest / V4, w4 = rest % V4;
+      *reinterpret_cast<u32x4 *>(lds_a + ((buf * KC + j) * kChunk + r) * AWP + 4 * w4) = ra[q];
+    }
+    if (tid < KC * kChunk) lds_nc[buf * KC * kChunk + tid] = rnc;
+  };
+
+  issue(0);
+  store(0);
+  __syncthreads();
+  for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+#pragma unroll
+          for (int w = 0; w < QW; ++w) bqc[nt][m][j][w] = bqn[nt][m][j][w];
+          bsc[nt][m][j] = bsn[nt][m][j];
+        }
+    if (c + 1 < nchunks) issue(c + 1);
+    const int buf = c & 1;
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      if (c * KC + j < nblocks) {
+        const uint32_t *la = lds_a + (buf * KC + j) * kChunk * AWP;
+        const float *ln = lds_nc + (buf * KC + j) * kChunk;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          bf16x8 bop[NM];
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            uint32_t pw[4];
+            decode_quad<FMT>(qd, bqc[nt][m][j], one, pw);
+            bop[m] = as_bf16x8(pw);
+          }
+#pragma unroll
+          for (int mt = 0; mt < kMT; ++mt) {
+            if (mt < nmt) {
+              bf16x8 av[NA];
+#pragma unroll
+              for (int v = 0; v < NA; ++v)
+                av[v] = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(la + (mt * 16 + col) * AWP + v * 16 + 4 * kq));
+              const floatx4 cin = *reinterpret_cast<const floatx4 *>(ln + mt * 16 + 4 * kq);
+#pragma unroll
+              for (int m = 0; m < NM; ++m) {
+                floatx4 pr = mfma(av[0], bop[m], cin);
+#pragma unroll
+                for (int v = 1; v < NA; ++v) pr = mfma(av[v], bop[m], pr);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  acc[mt][nt][m][i] = fmaf(bsc[nt][m][j], pr[i], acc[mt][nt][m][i]);
+              }
+            }
+          }
+        }
+      }
+    }
+    if (c + 1 < nchunks) store((c + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// LDS of the prefill products: the A staging buffers (also the h tiles of
+// the gate/up epilogue), the accumulator starts and the row table.
+constexpr int kLdsAWords = 2 * 4 * kChunk * 20;
+static_assert(2 * 2 * kChunk * 36 <= kLdsAWords, "down / fp32-x staging fits");
+static_assert(4 * kChunk * 32 <= kLdsAWords, "h tiles of four waves fit");
+
+__device__ __forceinline__ ExpertDesc pf_desc(const PfArgs &a, int e) {
+  const ExpertDesc *tab = reinterpret_cast<const ExpertDesc *>(a.image + kImgTable);
+  ExpertDesc ed;
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    ed.codes[m] = uniform64(tab[e].codes[m]);
+    ed.scales[m] = uniform64(tab[e].scales[m]);
+    ed.fmt[m] = uniform(tab[e].fmt[m]);
+  }
+  ed.reserved = 0;
+  return ed;
+}
+
+// ------------------------------------------------------------- gate / up
+
+// A workgroup covers kTileGU rows of gate and up: each wave two 16-row
+// tiles, i.e. one 32-row block of h, which it prepares for the down matrix
+// itself after the products (h staged in LDS, four waves at a time).
 template <int FMT, int VX>
 __device__ void pf_gateup_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed,
-                               float *hs /* [kChunk][64] */, float *ncs /* [2][kChunk] */,
-                               int *toks /* [kChunk] */) {
+                               uint32_t *lds_a, float *lds_nc, PfRows &rows) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4, col = lane & 15;
   const int e = tk.expert, m0 = tk.m0, cnt = tk.rows;
   const int nmt = (cnt + 15) >> 4;
   const int slot = a.fmt_slot[FMT];
-  const int n0 = blockIdx.x * kTileN;
-  const int my_row = n0 + 16 * wave + col;
-  for (int r = tid; r < kChunk; r += 256) toks[r] = r < cnt ? a.ltok[(size_t)e * a.T + m0 + r] : 0;
-  __syncthreads();
-  const __amdgpu_buffer_rsrc_t img = make_rsrc(a.image, (uint32_t)a.image_bytes);
-  const __amdgpu_buffer_rsrc_t xpr =
-      make_rsrc(a.xp, (uint32_t)((size_t)__builtin_popcount(a.gu_fmts) * a.T * a.nb_d * a.vx * 64));
-  QuadDecode<FMT> qd;
-  qd.init(kq);
-  const uint32_t cb = code_bytes(FMT), sb = scale_bytes(FMT);
-  uint32_t coff[2], soff[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    coff[m] = (uint32_t)(ed.codes[m] + (size_t)my_row * a.nb_d * cb);
-    soff[m] = (uint32_t)(ed.scales[m] + (size_t)my_row * a.nb_d * sb);
+  const int n0 = blockIdx.x * kTileGU;
+  for (int r = tid; r < kChunk; r += kPfThreads) {
+    const int tok = a.ltok[(size_t)e * a.T + m0 + (r < cnt ? r : 0)];
+    rows.a_row[r] = (uint32_t)(((size_t)slot * a.T + tok) * a.nb_d * VX * 64);
+    rows.nc_row[r] = (uint32_t)(((size_t)slot * a.nb_d * a.T + tok) * 4);
   }
-  int tokA[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) tokA[mt] = toks[mt * 16 + col];
-  floatx4 acc[kMT][2];
+  __syncthreads();
+  const size_t nf = __builtin_popcount(a.gu_fmts);
+  const __amdgpu_buffer_rsrc_t xpr = make_rsrc(a.xp, (uint32_t)(nf * a.T * a.nb_d * VX * 64));
+  const __amdgpu_buffer_rsrc_t ncr = make_rsrc(a.xnc, (uint32_t)(nf * a.nb_d * a.T * 4));
+  floatx4 acc[kMT][2][2];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-    for (int m = 0; m < 2; ++m) acc[mt][m] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const uint32_t one = one_one_vgpr();
-  const float *xnc = a.xnc + (size_t)slot * a.nb_d * a.T;
-  // accumulator starts of block 0
-  for (int r = tid; r < cnt; r += 256) ncs[r] = xnc[toks[r]];
-  __syncthreads();
-  for (int b = 0; b < a.nb_d; ++b) {
-    float *ncb = ncs + (b & 1) * kChunk;
-    if (b + 1 < a.nb_d) {
-      float *ncn = ncs + ((b + 1) & 1) * kChunk;
-      for (int r = tid; r < cnt; r += 256) ncn[r] = xnc[(size_t)(b + 1) * a.T + toks[r]];
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) acc[mt][nt][m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // this wave's 32 rows = one block of h; a wave past the end of a ragged
+  // last tile computes rows 0..31 again and stores nothing
+  const bool active = n0 + 32 * wave < a.f;
+  const int row0 = active ? n0 + 32 * wave : 0;
+  pf_gemm<FMT, 2, 2, VX, (VX == 1 ? 4 : 2)>(a, a.nb_d, nmt, xpr, VX * 64, ncr, a.T * 4, rows,
+                                             ed, 0, row0, a.nb_d, lds_a, lds_nc, acc);
+  // h of this wave's block, prepared for the down matrix; LDS holds the h
+  // tiles of four waves at a time ([4][kChunk][32] floats)
+  const int fdn = ed.fmt[2];
+  const int rowbase = a.offs[e] + m0;
+  const int fbg = row0 / 32;
+  float *hall = reinterpret_cast<float *>(lds_a);
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    const bool mine = active && (wave >> 2) == round;
+    float *hs = hall + (wave & 3) * kChunk * 32;
+    if (mine) {
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt)
+        if (mt < nmt)
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              hs[(mt * 16 + 4 * kq + i) * 32 + 16 * nt + col] =
+                  silu(acc[mt][nt][0][i]) * acc[mt][nt][1][i];
     }
-    bf16x8 bop[2];
-    float sc[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      uint32_t q[3], pw[4];
-      load_quad<FMT>(img, coff[m] + b * cb, qd, q);
-      sc[m] = load_block_scale<FMT>(img, soff[m] + b * sb);
-      decode_quad<FMT>(qd, q, one, pw);
-      bop[m] = as_bf16x8(pw);
-    }
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-      if (mt < nmt) {
-        const uint32_t xoff =
-            (uint32_t)((((size_t)slot * a.T + tokA[mt]) * a.nb_d + b) * a.vx * 64 + 16 * kq);
-        const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(xpr, (int)xoff, 0, 0);
-        const floatx4 c = *reinterpret_cast<const floatx4 *>(ncb + mt * 16 + 4 * kq);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a0);
-        bf16x8 av1 = av;
-        if constexpr (VX == 2)
-          av1 = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xpr, (int)(xoff + 64), 0, 0));
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          floatx4 p = mfma(av, bop[m], c);
-          if constexpr (VX == 2) p = mfma(av1, bop[m], p);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][m][i] = fmaf(sc[m], p[i], acc[mt][m][i]);
+    __syncthreads();
+    if (mine) {
+      // 16 lanes per (row, block): four rows per pass of the wave
+      for (int r0 = 0; r0 < cnt; r0 += 4) {
+        const int r = r0 + (lane >> 4), p = lane & 15;
+        float share = 0.f;
+        const size_t hrow = (size_t)rowbase + r;
+        if (r < cnt) {
+          uint32_t *dst = a.hp + (hrow * a.nb_f + fbg) * 32;
+          share = prep_h_pair_rt(fdn, hs + r * 32, p, dst);
         }
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
+        if (r < cnt && p == 0) a.hnc[(size_t)fbg * (a.rows_max + 16) + hrow] = share;
       }
     }
     __syncthreads();
   }
-  // h = silu(g) * u into LDS: rows m = 16 mt + 4 kq + i, column 16 wave + col
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt)
-    if (mt < nmt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        hs[(mt * 16 + 4 * kq + i) * kTileN + 16 * wave + col] = silu(acc[mt][0][i]) * acc[mt][1][i];
-  __syncthreads();
-  // prepare h for the down matrix: 16 threads per (row, f-block)
-  const int fdn = ed.fmt[2];
-  const int nfb = kTileN / 32;
-  const int nitems = cnt * nfb * 16;
-  const int rowbase = a.offs[e] + m0;
-  for (int base = 0; base < nitems; base += 256) {
-    const int it = base + tid;
-    float share = 0.f;
-    size_t hrow = 0;
-    int fbg = 0;
-    if (it < nitems) {
-      const int p = it & 15, rb = it >> 4;
-      const int r = rb / nfb, fb = rb % nfb;
-      fbg = n0 / 32 + fb;
-      hrow = (size_t)rowbase + r;
-      const float *hblk = hs + r * kTileN + 32 * fb;
-      uint32_t *dst = a.hp + (hrow * a.nb_f + fbg) * 32;
-      share = prep_h_pair_rt(fdn, hblk, p, dst);
-    }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
-    if (it < nitems && (it & 15) == 0) a.hnc[(size_t)fbg * (a.rows_max + 16) + hrow] = share;
-  }
 }
 
 template <int VX>
-__global__ __launch_bounds__(256) void k_pf_gateup(PfArgs a) {
+__global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PfArgs a) {
   if ((int)blockIdx.y >= a.ntasks[0]) return;
   const PfTask tk = a.tasks[blockIdx.y];
-  __shared__ __align__(16) float hs[kChunk * kTileN];
-  __shared__ __align__(16) float ncs[2 * kChunk];
-  __shared__ int toks[kChunk];
-  const ExpertDesc *tab = reinterpret_cast<const ExpertDesc *>(a.image + kImgTable);
-  ExpertDesc ed;
-#pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    ed.codes[m] = uniform64(tab[tk.expert].codes[m]);
-    ed.scales[m] = uniform64(tab[tk.expert].scales[m]);
-    ed.fmt[m] = uniform(tab[tk.expert].fmt[m]);
-  }
+  __shared__ __align__(16) uint32_t lds_a[kLdsAWords];
+  __shared__ __align__(16) float lds_nc[2 * 4 * kChunk];
+  __shared__ PfRows rows;
+  const ExpertDesc ed = pf_desc(a, tk.expert);
   const int fmt = ed.fmt[0];
-  if (fmt == RFPX_FP2) pf_gateup_task<RFPX_FP2, VX>(a, tk, ed, hs, ncs, toks);
-  else if (fmt == RFPX_FP3) pf_gateup_task<RFPX_FP3, VX>(a, tk, ed, hs, ncs, toks);
-  else pf_gateup_task<RFPX_FP4, VX>(a, tk, ed, hs, ncs, toks);
+  if (fmt == RFPX_FP2) pf_gateup_task<RFPX_FP2, VX>(a, tk, ed, lds_a, lds_nc, rows);
+  else if (fmt == RFPX_FP3) pf_gateup_task<RFPX_FP3, VX>(a, tk, ed, lds_a, lds_nc, rows);
+  else pf_gateup_task<RFPX_FP4, VX>(a, tk, ed, lds_a, lds_nc, rows);
 }
 
 // ------------------------------------------------------------------- down
 
+// A workgroup covers kTileDN rows of the down matrix: four 16-row tiles per
+// wave.
 template <int FMT>
-__device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed) {
+__device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed,
+                             uint32_t *lds_a, float *lds_nc, PfRows &rows) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4, col = lane & 15;
   const int e = tk.expert, m0 = tk.m0, cnt = tk.rows;
   const int nmt = (cnt + 15) >> 4;
-  const int n0 = blockIdx.x * kTileN;
-  const int my_row = n0 + 16 * wave + col;
+  const bool active = (int)blockIdx.x * kTileDN + 64 * wave < a.d;  // see pf_gateup_task
+  const int row0 = active ? (int)blockIdx.x * kTileDN + 64 * wave : 0;
   const int rowbase = a.offs[e] + m0;
-  const __amdgpu_buffer_rsrc_t img = make_rsrc(a.image, (uint32_t)a.image_bytes);
-  const size_t hp_bytes = (size_t)(a.rows_max + 16) * a.nb_f * 128;
-  const __amdgpu_buffer_rsrc_t hpr = make_rsrc(a.hp, (uint32_t)hp_bytes);
-  const __amdgpu_buffer_rsrc_t hncr =
-      make_rsrc(a.hnc, (uint32_t)((size_t)a.nb_f * (a.rows_max + 16) * 4));
-  QuadDecode<FMT> qd;
-  qd.init(kq);
-  const uint32_t cb = code_bytes(FMT), sb = scale_bytes(FMT);
-  const uint32_t coff = (uint32_t)(ed.codes[2] + (size_t)my_row * a.nb_f * cb);
-  const uint32_t soff = (uint32_t)(ed.scales[2] + (size_t)my_row * a.nb_f * sb);
-  floatx4 acc[kMT];
-#pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) acc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  const uint32_t one = one_one_vgpr();
-  for (int b = 0; b < a.nb_f; ++b) {
-    uint32_t q[3], pw[4];
-    load_quad<FMT>(img, coff + b * cb, qd, q);
-    const float sc = load_block_scale<FMT>(img, soff + b * sb);
-    decode_quad<FMT>(qd, q, one, pw);
-    const bf16x8 bop = as_bf16x8(pw);
-    const uint32_t hncb = (uint32_t)(((size_t)b * (a.rows_max + 16) + rowbase) * 4);
-#pragma unroll
-    for (int mt = 0; mt < kMT; ++mt) {
-      if (mt < nmt) {
-        const uint32_t hoff =
-            (uint32_t)((((size_t)rowbase + mt * 16 + col) * a.nb_f + b) * 128 + 16 * kq);
-        const u32x4 ahi = __builtin_amdgcn_raw_buffer_load_b128(hpr, (int)hoff, 0, 0);
-        const u32x4 alo = __builtin_amdgcn_raw_buffer_load_b128(hpr, (int)(hoff + 64), 0, 0);
-        const floatx4 c = __builtin_bit_cast(
-            floatx4, __builtin_amdgcn_raw_buffer_load_b128(hncr, (int)(hncb + 4 * (mt * 16 + 4 * kq)), 0, 0));
-        floatx4 p = mfma(__builtin_bit_cast(bf16x8, ahi), bop, c);
-        p = mfma(__builtin_bit_cast(bf16x8, alo), bop, p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] = fmaf(sc, p[i], acc[mt][i]);
-      }
-    }
+  for (int r = tid; r < kChunk; r += kPfThreads) {
+    const size_t row = (size_t)rowbase + (r < cnt ? r : 0);
+    rows.a_row[r] = (uint32_t)(row * a.nb_f * 128);
+    rows.nc_row[r] = (uint32_t)(row * 4);
   }
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t hpr =
+      make_rsrc(a.hp, (uint32_t)((size_t)(a.rows_max + 16) * a.nb_f * 128));
+  const __amdgpu_buffer_rsrc_t ncr =
+      make_rsrc(a.hnc, (uint32_t)((size_t)a.nb_f * (a.rows_max + 16) * 4));
+  floatx4 acc[kMT][4][1];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) acc[mt][nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+  pf_gemm<FMT, 1, 4, 2, 2>(a, a.nb_f, nmt, hpr, 128, ncr, (a.rows_max + 16) * 4, rows, ed, 2,
+                           row0, a.nb_f, lds_a, lds_nc, acc);
   const int *ltok = a.ltok + (size_t)e * a.T + m0;
   const int *lrank = a.lrank + (size_t)e * a.T + m0;
   const float *lw = a.lw + (size_t)e * a.T + m0;
@@ -592,28 +703,27 @@ __device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = mt * 16 + 4 * kq + i;
-        if (r < cnt) {
+        if (active && r < cnt) {
           const int t = ltok[r];
-          a.out[((size_t)t * (a.k + 1) + lrank[r]) * a.d + my_row] = lw[r] * acc[mt][i];
+          float *o = a.out + ((size_t)t * (a.k + 1) + lrank[r]) * a.d + row0 + col;
+          const float w = lw[r];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) o[16 * nt] = w * acc[mt][nt][0][i];
         }
       }
 }
 
-__global__ __launch_bounds__(256) void k_pf_down(PfArgs a) {
+__global__ __launch_bounds__(kPfThreads) void k_pf_down(PfArgs a) {
   if ((int)blockIdx.y >= a.ntasks[0]) return;
   const PfTask tk = a.tasks[blockIdx.y];
-  const ExpertDesc *tab = reinterpret_cast<const ExpertDesc *>(a.image + kImgTable);
-  ExpertDesc ed;
-#pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    ed.codes[m] = uniform64(tab[tk.expert].codes[m]);
-    ed.scales[m] = uniform64(tab[tk.expert].scales[m]);
-    ed.fmt[m] = uniform(tab[tk.expert].fmt[m]);
-  }
+  __shared__ __align__(16) uint32_t lds_a[kLdsAWords];
+  __shared__ __align__(16) float lds_nc[2 * 4 * kChunk];
+  __shared__ PfRows rows;
+  const ExpertDesc ed = pf_desc(a, tk.expert);
   const int fmt = ed.fmt[2];
-  if (fmt == RFPX_FP2) pf_down_task<RFPX_FP2>(a, tk, ed);
-  else if (fmt == RFPX_FP3) pf_down_task<RFPX_FP3>(a, tk, ed);
-  else pf_down_task<RFPX_FP4>(a, tk, ed);
+  if (fmt == RFPX_FP2) pf_down_task<RFPX_FP2>(a, tk, ed, lds_a, lds_nc, rows);
+  else if (fmt == RFPX_FP3) pf_down_task<RFPX_FP3>(a, tk, ed, lds_a, lds_nc, rows);
+  else pf_down_task<RFPX_FP4>(a, tk, ed, lds_a, lds_nc, rows);
 }
 
 // ---------------------------------------------------------------- combine
@@ -652,7 +762,7 @@ size_t prefill_layout(const moe_layer *L, int T, int xtype, void *args_out) {
   for (int e = 0; e <= L->n_experts; ++e) a.gu_fmts |= 1u << L->fmts[3 * e];
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
     if ((a.gu_fmts >> f) & 1u) a.fmt_slot[f] = nf++;
-  if (L->d % kTileN || L->f % kTileN) return 0;
+  if (L->d % 64 || L->f % 64) return 0;
   const size_t E1 = L->n_experts + 1;
   size_t off = 0;
   struct Item {
@@ -741,10 +851,11 @@ hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, f
   k_pf_group<<<a.E + 1, 256, 0, stream>>>(a);
   k_pf_plan<<<1, 1024, 0, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 ggu(a.f / kTileN, a.max_tasks), gdn(a.d / kTileN, a.max_tasks);
-  if (a.vx == 1) k_pf_gateup<1><<<ggu, 256, 0, stream>>>(a);
-  else k_pf_gateup<2><<<ggu, 256, 0, stream>>>(a);
-  k_pf_down<<<gdn, 256, 0, stream>>>(a);
+  const dim3 ggu((a.f + kTileGU - 1) / kTileGU, a.max_tasks);
+  const dim3 gdn((a.d + kTileDN - 1) / kTileDN, a.max_tasks);
+  if (a.vx == 1) k_pf_gateup<1><<<ggu, kPfThreads, 0, stream>>>(a);
+  else k_pf_gateup<2><<<ggu, kPfThreads, 0, stream>>>(a);
+  k_pf_down<<<gdn, kPfThreads, 0, stream>>>(a);
   k_pf_combine<<<(unsigned)(((size_t)T * a.d + 255) / 256), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
