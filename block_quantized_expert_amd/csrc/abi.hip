@@ -265,8 +265,9 @@ rfpx_status moe_prefill_forward(const moe_layer *L, const void *x, int xtype, in
   if (st) return st;
   if (xtype != RFPX_X_F32 && xtype != RFPX_X_BF16) return fail(RFPX_E_ARG, "xtype=%d", xtype);
   if (T < 1 || T > 65536) return fail(RFPX_E_SHAPE, "T=%d: must be in [1, 65536]", T);
-  if (L->d % 64 || L->f % 64)
-    return fail(RFPX_E_SHAPE, "prefill needs d and f multiples of 64 (d=%d, f=%d)", L->d, L->f);
+  if (L->d % 128 || L->f % 64)
+    return fail(RFPX_E_SHAPE, "prefill needs d a multiple of 128 and f of 64 (d=%d, f=%d)",
+                L->d, L->f);
   const size_t need = prefill_layout(L, T, xtype, nullptr);
   if (!need) return fail(RFPX_E_SHAPE, "prefill: unsupported shape (T=%d)", T);
   if (!L->router_w || !L->image) return fail(RFPX_E_ARG, "layer router or image is null");

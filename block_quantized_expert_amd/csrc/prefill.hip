@@ -43,10 +43,12 @@ namespace rfpx {
 namespace {
 
 constexpr int kChunk = 64;      // rows (tokens) per task
-constexpr int kPfThreads = 512; // 8 waves per product workgroup
-constexpr int kTileGU = 256;    // gate/up rows per workgroup: 8 waves x 2 x 16
-constexpr int kTileDN = 512;    // down rows per workgroup: 8 waves x 4 x 16
+constexpr int kPfWaves = 4;     // waves per product workgroup
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kTileGU = 64;     // gate/up rows per workgroup: 4 waves x 16 (of gate and of up)
+constexpr int kTileDN = 128;    // down rows per workgroup: 4 waves x 2 x 16
 constexpr int kMT = kChunk / 16;
+constexpr int kXcds = 8;        // accelerator complex dies of the chip
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
@@ -415,54 +417,127 @@ struct PfRows {
   uint32_t nc_row[kChunk];
 };
 
+// Weight rows staged in LDS.  Every wave owns kRowsPerWave rows of B (16
+// rows x NT tiles x NM matrices) and a private LDS region holding a span of
+// SB consecutive blocks of each of them: the codes, then the scales, each
+// loaded as whole 16-byte pieces starting at the 16-byte boundary at or
+// below the span (so a row's cache lines are consumed whole, not a few
+// bytes per block as in a per-lane read of the MFMA operand layout).  A row
+// of the region: 16 bytes of slack (an FP3 lane reads from 4 bytes before
+// its block), then the pieces; the pitch is an odd multiple of 16 bytes,
+// which spreads the 16 rows one read touches over the LDS banks.
+constexpr int kRowsPerWave = 32;
+
+template <int FMT>
+struct BStage {
+  static constexpr int CB = FMT == RFPX_FP2 ? 8 : FMT == RFPX_FP3 ? 12 : 16;  // code bytes
+  static constexpr int SBY = FMT == RFPX_FP4 ? 1 : 2;                          // scale bytes
+  static constexpr int SB = FMT == RFPX_FP4 ? 8 : 16;                          // blocks per span
+  static constexpr int NPC = (15 + SB * CB + 15) / 16;                        // code pieces
+  static constexpr int NPS = (15 + SB * SBY + 15) / 16;                       // scale pieces
+  static constexpr int P = NPC + NPS;
+  static constexpr int PITCH0 = 16 + 16 * P;
+  static constexpr int PITCH = (PITCH0 / 16) % 2 ? PITCH0 : PITCH0 + 16;     // bytes
+  static constexpr int NB = (kRowsPerWave * P + 63) / 64;                     // b128 per lane
+};
+constexpr int kBRegionBytes =
+    kRowsPerWave * (BStage<RFPX_FP3>::PITCH > BStage<RFPX_FP2>::PITCH
+                        ? (BStage<RFPX_FP3>::PITCH > BStage<RFPX_FP4>::PITCH ? BStage<RFPX_FP3>::PITCH
+                                                                             : BStage<RFPX_FP4>::PITCH)
+                        : (BStage<RFPX_FP2>::PITCH > BStage<RFPX_FP4>::PITCH ? BStage<RFPX_FP2>::PITCH
+                                                                             : BStage<RFPX_FP4>::PITCH));
+
 // Output tile of a grouped product over nblocks blocks of 32: the task's
-// rows (at most kChunk) x NT 16-row tiles of NM matrices per wave, 8 waves
-// per workgroup.  Software-pipelined in chunks of KC blocks: while chunk c
-// is multiplied, the A words (and accumulator starts) of chunk c+1 are in
-// flight to registers, to be stored to the other LDS buffer, and the B code
-// words and scales of chunk c+1 to registers.  The A tile in LDS serves all
-// 8 x NT column tiles, so each A row is read from memory once per 128 NT
-// output rows.  NA = number of A terms per block (1, or 2 for bf16 hi +
-// lo), chained through the MFMA accumulator.
+// rows (at most kChunk) x NT 16-row tiles of NM matrices per wave.
+// Software-pipelined in chunks of KC blocks: while chunk c is multiplied,
+// the A words (and accumulator starts) of chunk c+1 are in flight to
+// registers, to be stored to the other LDS buffer.  The B span of the
+// wave's rows is refilled from registers every SB/KC chunks, and the next
+// span is then requested.  NA = number of A terms per block (1, or 2 for
+// bf16 hi + lo), chained through the MFMA accumulator.
 template <int FMT, int NM, int NT, int NA, int KC>
 __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
                                         __amdgpu_buffer_rsrc_t ar, uint32_t a_stride,
                                         __amdgpu_buffer_rsrc_t ncr, uint32_t nc_stride,
                                         const PfRows &rows, const ExpertDesc &ed, int mat0,
                                         int row0 /* first B row of this wave */, int nbB,
-                                        uint32_t *lds_a, float *lds_nc,
+                                        uint32_t *lds_a, float *lds_nc, uint8_t *lds_b,
                                         floatx4 (&acc)[kMT][NT][NM]) {
+  using BS = BStage<FMT>;
+  static_assert(16 * NT * NM == kRowsPerWave, "a wave owns kRowsPerWave rows of B");
+  static_assert(NM <= 2, "plane offsets are selected for at most two matrices");
+  static_assert(BS::SB % KC == 0, "a B span holds whole chunks");
   constexpr int AW = NA * 16, AWP = AW + 4, V4 = AW / 4;
-  constexpr int NLD = KC * kChunk * V4 / kPfThreads;
-  static_assert(NLD * kPfThreads == KC * kChunk * V4, "A loads must split evenly");
-  constexpr int QW = FMT == RFPX_FP3 ? 3 : 1;
+  constexpr int PPR = KC * V4;  // 16-byte pieces of one A row per chunk
+  static_assert(PPR == 16, "16 lanes per A row");
+  constexpr int NLD = kChunk * PPR / kPfThreads;
+  constexpr int CPS = BS::SB / KC;  // chunks per B span
   const int tid = threadIdx.x, lane = tid & 63, kq = lane >> 4, col = lane & 15;
   QuadDecode<FMT> qd;
   qd.init(kq);
   const __amdgpu_buffer_rsrc_t img = make_rsrc(a.image, (uint32_t)a.image_bytes);
-  const uint32_t cb = code_bytes(FMT), sb = scale_bytes(FMT);
-  uint32_t coff[NT][NM], soff[NT][NM];
+  const uint32_t rstride_c = (uint32_t)nbB * BS::CB, rstride_s = (uint32_t)nbB * BS::SBY;
+  // this lane's LDS read addresses (bytes) of each (tile, matrix)
+  uint32_t lc[NT][NM], ls[NT][NM];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      const size_t row = (size_t)row0 + 16 * nt + col;
-      coff[nt][m] = (uint32_t)(ed.codes[mat0 + m] + row * nbB * cb);
-      soff[nt][m] = (uint32_t)(ed.scales[mat0 + m] + row * nbB * sb);
+      const uint32_t row = (uint32_t)(row0 + 16 * nt + col);
+      const uint32_t rr = (uint32_t)(m * 16 * NT + 16 * nt + col);
+      lc[nt][m] = rr * BS::PITCH + 16 + (row * rstride_c) % 16 + 4 * qd.word;
+      ls[nt][m] = rr * BS::PITCH + 16 + 16 * BS::NPC + (row * rstride_s) % 16;
+      // (a span of codes is a whole number of 16-byte pieces, so a row's
+      // code offset in its first piece is the same for every span; the
+      // scale offset of an FP4 span of 8 bytes alternates, see below)
     }
   const int nchunks = (nblocks + KC - 1) / KC;
+  const int nspans = (nblocks + BS::SB - 1) / BS::SB;
   u32x4 ra[NLD];
   float rnc = 0.f;
-  uint32_t bqn[NT][NM][KC][QW], bqc[NT][NM][KC][QW];
-  float bsn[NT][NM][KC], bsc[NT][NM][KC];
-  const uint32_t one = one_one_vgpr();
+  u32x4 rb[BS::NB];
 
-  auto issue = [&](int c) {
+  auto issue_b = [&](int sp) {
+#pragma unroll
+    for (int q = 0; q < BS::NB; ++q) {
+      const int item = lane + 64 * q;
+      const int rr = min(item / BS::P, kRowsPerWave - 1), p = item % BS::P;
+      const int row = row0 + rr % (16 * NT);
+      // plane offsets of the row's matrix (selects: no indexed register array)
+      const bool m1 = NM > 1 && rr >= 16 * NT;
+      const uint32_t cbase = (uint32_t)(m1 ? ed.codes[mat0 + 1] : ed.codes[mat0]);
+      const uint32_t sbase = (uint32_t)(m1 ? ed.scales[mat0 + 1] : ed.scales[mat0]);
+      uint32_t off, span;
+      int pp;
+      if (p < BS::NPC) {
+        off = cbase + row * rstride_c + sp * (BS::SB * BS::CB);
+        span = BS::SB * BS::CB;
+        pp = p;
+      } else {
+        off = sbase + row * rstride_s + sp * (BS::SB * BS::SBY);
+        span = BS::SB * BS::SBY;
+        pp = p - BS::NPC;
+      }
+      const bool need = item < kRowsPerWave * BS::P && 16u * pp < (off & 15u) + span;
+      rb[q] = need ? __builtin_amdgcn_raw_buffer_load_b128(img, (int)((off & ~15u) + 16 * pp), 0, 0)
+                   : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_b = [&]() {
+#pragma unroll
+    for (int q = 0; q < BS::NB; ++q) {
+      const int item = lane + 64 * q;
+      const int rr = item / BS::P, p = item % BS::P;
+      if (item < kRowsPerWave * BS::P)
+        *reinterpret_cast<u32x4 *>(lds_b + rr * BS::PITCH + 16 + 16 * p) = rb[q];
+    }
+  };
+  auto issue_a = [&](int c) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int item = tid + kPfThreads * q;
-      const int r = item % kChunk, rest = item / kChunk;
-      const int j = rest / V4, w4 = rest % V4;
+      const int r = item / PPR, pc = item % PPR;
+      const int j = pc / V4, w4 = pc % V4;
       const int blk = min(c * KC + j, nblocks - 1);
       ra[q] = __builtin_amdgcn_raw_buffer_load_b128(
           ar, (int)(rows.a_row[r] + blk * a_stride + 16 * w4), 0, 0);
@@ -473,57 +548,56 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
       rnc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                           ncr, (int)(rows.nc_row[r] + blk * nc_stride), 0, 0));
     }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int j = 0; j < KC; ++j) {
-          const uint32_t blk = (uint32_t)min(c * KC + j, nblocks - 1);
-          load_quad<FMT>(img, coff[nt][m] + blk * cb, qd, bqn[nt][m][j]);
-          bsn[nt][m][j] = load_block_scale<FMT>(img, soff[nt][m] + blk * sb);
-        }
   };
-  auto store = [&](int buf) {
+  auto store_a = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int item = tid + kPfThreads * q;
-      const int r = item % kChunk, rest = item / kChunk;
-      const int j = rest / V4, w4 = rest % V4;
+      const int r = item / PPR, pc = item % PPR;
+      const int j = pc / V4, w4 = pc % V4;
       *reinterpret_cast<u32x4 *>(lds_a + ((buf * KC + j) * kChunk + r) * AWP + 4 * w4) = ra[q];
     }
     if (tid < KC * kChunk) lds_nc[buf * KC * kChunk + tid] = rnc;
   };
 
-  issue(0);
-  store(0);
+  issue_b(0);
+  issue_a(0);
+  store_b();
+  if (nspans > 1) issue_b(1);
+  store_a(0);
   __syncthreads();
+  const uint32_t one = one_one_vgpr();
   for (int c = 0; c < nchunks; ++c) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-#pragma unroll
-        for (int j = 0; j < KC; ++j) {
-#pragma unroll
-          for (int w = 0; w < QW; ++w) bqc[nt][m][j][w] = bqn[nt][m][j][w];
-          bsc[nt][m][j] = bsn[nt][m][j];
-        }
-    if (c + 1 < nchunks) issue(c + 1);
+    if (c + 1 < nchunks) issue_a(c + 1);
     const int buf = c & 1;
+    const int jb0 = (c % CPS) * KC;
+    // shift of this span's scales within their first piece
+    const uint32_t sadd = (BS::SB * BS::SBY) % 16 ? (uint32_t)((c / CPS) * BS::SB * BS::SBY) % 16 : 0u;
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
       if (c * KC + j < nblocks) {
         const uint32_t *la = lds_a + (buf * KC + j) * kChunk * AWP;
         const float *ln = lds_nc + (buf * KC + j) * kChunk;
+        const int jb = jb0 + j;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           bf16x8 bop[NM];
+          float bs[NM];
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
-            uint32_t pw[4];
-            decode_quad<FMT>(qd, bqc[nt][m][j], one, pw);
+            const uint8_t *cp = lds_b + lc[nt][m] + jb * BS::CB;
+            uint32_t q[3], pw[4];
+            q[0] = *reinterpret_cast<const uint32_t *>(cp);
+            if (FMT == RFPX_FP3) {
+              q[1] = *reinterpret_cast<const uint32_t *>(cp + 4);
+              q[2] = *reinterpret_cast<const uint32_t *>(cp + 8);
+            }
+            decode_quad<FMT>(qd, q, one, pw);
             bop[m] = as_bf16x8(pw);
+            const uint32_t lsr = ls[nt][m] - (ls[nt][m] & 15u) + (((ls[nt][m] & 15u) + sadd) & 15u);
+            const uint8_t *sp = lds_b + lsr + jb * BS::SBY;
+            bs[m] = FMT == RFPX_FP4 ? block_scale<RFPX_FP4>(*sp)
+                                    : block_scale<FMT>(*reinterpret_cast<const uint16_t *>(sp));
           }
 #pragma unroll
           for (int mt = 0; mt < kMT; ++mt) {
@@ -540,24 +614,39 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
 #pragma unroll
                 for (int v = 1; v < NA; ++v) pr = mfma(av[v], bop[m], pr);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  acc[mt][nt][m][i] = fmaf(bsc[nt][m][j], pr[i], acc[mt][nt][m][i]);
+                for (int i = 0; i < 4; ++i) acc[mt][nt][m][i] = fmaf(bs[m], pr[i], acc[mt][nt][m][i]);
               }
             }
           }
         }
       }
     }
-    if (c + 1 < nchunks) store((c + 1) & 1);
+    if (c + 1 < nchunks) {
+      store_a((c + 1) & 1);
+      if ((c + 1) % CPS == 0) {
+        // this wave has finished with its span: refill it, ask for the next
+        const int sp = (c + 1) / CPS;
+        store_b();
+        if (sp + 1 < nspans) issue_b(sp + 1);
+      }
+    }
     __syncthreads();
   }
 }
 
-// LDS of the prefill products: the A staging buffers (also the h tiles of
-// the gate/up epilogue), the accumulator starts and the row table.
+// LDS of the prefill products: the A staging buffers (also the h tile of
+// the gate/up epilogue), the accumulator starts, the B regions of the
+// waves and the row table.
 constexpr int kLdsAWords = 2 * 4 * kChunk * 20;
 static_assert(2 * 2 * kChunk * 36 <= kLdsAWords, "down / fp32-x staging fits");
-static_assert(4 * kChunk * 32 <= kLdsAWords, "h tiles of four waves fit");
+static_assert(kChunk * kTileGU <= kLdsAWords, "h tile fits");
+
+struct PfLds {
+  uint32_t a[kLdsAWords];
+  float nc[2 * 4 * kChunk];
+  uint8_t b[kPfWaves][kBRegionBytes];
+  PfRows rows;
+};
 
 __device__ __forceinline__ ExpertDesc pf_desc(const PfArgs &a, int e) {
   const ExpertDesc *tab = reinterpret_cast<const ExpertDesc *>(a.image + kImgTable);
@@ -572,128 +661,119 @@ __device__ __forceinline__ ExpertDesc pf_desc(const PfArgs &a, int e) {
   return ed;
 }
 
+// Workgroup -> (task, column slice).  Workgroups are handed to the XCDs in
+// turn (workgroup n to XCD n mod 8), so the slices of task t are numbered
+// to land on XCD t mod 8 together: the task's A rows are then fetched into
+// one L2 only.
+__device__ __forceinline__ bool pf_work(const PfArgs &a, int nslices, int *task, int *slice) {
+  const int n = blockIdx.x, xcd = n % kXcds, local = n / kXcds;
+  const int t = xcd + kXcds * (local / nslices);
+  *slice = local % nslices;
+  *task = t;
+  return t < a.ntasks[0];
+}
+
 // ------------------------------------------------------------- gate / up
 
-// A workgroup covers kTileGU rows of gate and up: each wave two 16-row
-// tiles, i.e. one 32-row block of h, which it prepares for the down matrix
-// itself after the products (h staged in LDS, four waves at a time).
+// A workgroup covers kTileGU rows of gate and of up: each wave one 16-row
+// tile of both.  After the products the h tile goes through LDS, and the
+// workgroup prepares its kTileGU / 32 blocks of h for the down matrix.
 template <int FMT, int VX>
-__device__ void pf_gateup_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed,
-                               uint32_t *lds_a, float *lds_nc, PfRows &rows) {
+__device__ void pf_gateup_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed, int slice,
+                               PfLds &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4, col = lane & 15;
   const int e = tk.expert, m0 = tk.m0, cnt = tk.rows;
   const int nmt = (cnt + 15) >> 4;
   const int slot = a.fmt_slot[FMT];
-  const int n0 = blockIdx.x * kTileGU;
+  const int n0 = slice * kTileGU;
   for (int r = tid; r < kChunk; r += kPfThreads) {
     const int tok = a.ltok[(size_t)e * a.T + m0 + (r < cnt ? r : 0)];
-    rows.a_row[r] = (uint32_t)(((size_t)slot * a.T + tok) * a.nb_d * VX * 64);
-    rows.nc_row[r] = (uint32_t)(((size_t)slot * a.nb_d * a.T + tok) * 4);
+    sm.rows.a_row[r] = (uint32_t)(((size_t)slot * a.T + tok) * a.nb_d * VX * 64);
+    sm.rows.nc_row[r] = (uint32_t)(((size_t)slot * a.nb_d * a.T + tok) * 4);
   }
   __syncthreads();
   const size_t nf = __builtin_popcount(a.gu_fmts);
   const __amdgpu_buffer_rsrc_t xpr = make_rsrc(a.xp, (uint32_t)(nf * a.T * a.nb_d * VX * 64));
   const __amdgpu_buffer_rsrc_t ncr = make_rsrc(a.xnc, (uint32_t)(nf * a.nb_d * a.T * 4));
-  floatx4 acc[kMT][2][2];
+  floatx4 acc[kMT][1][2];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int m = 0; m < 2; ++m) acc[mt][0][m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int row0 = n0 + 16 * wave;
+  pf_gemm<FMT, 2, 1, VX, (VX == 1 ? 4 : 2)>(a, a.nb_d, nmt, xpr, VX * 64, ncr, a.T * 4, sm.rows,
+                                             ed, 0, row0, a.nb_d, sm.a, sm.nc, sm.b[wave], acc);
+  // h tile [kChunk][kTileGU] in LDS, then h prepared for the down matrix:
+  // 16 lanes per (row, block of 32)
+  float *hs = reinterpret_cast<float *>(sm.a);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) acc[mt][nt][m] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // this wave's 32 rows = one block of h; a wave past the end of a ragged
-  // last tile computes rows 0..31 again and stores nothing
-  const bool active = n0 + 32 * wave < a.f;
-  const int row0 = active ? n0 + 32 * wave : 0;
-  pf_gemm<FMT, 2, 2, VX, (VX == 1 ? 4 : 2)>(a, a.nb_d, nmt, xpr, VX * 64, ncr, a.T * 4, rows,
-                                             ed, 0, row0, a.nb_d, lds_a, lds_nc, acc);
-  // h of this wave's block, prepared for the down matrix; LDS holds the h
-  // tiles of four waves at a time ([4][kChunk][32] floats)
+  for (int mt = 0; mt < kMT; ++mt)
+    if (mt < nmt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hs[(mt * 16 + 4 * kq + i) * kTileGU + 16 * wave + col] =
+            silu(acc[mt][0][0][i]) * acc[mt][0][1][i];
+  __syncthreads();
   const int fdn = ed.fmt[2];
   const int rowbase = a.offs[e] + m0;
-  const int fbg = row0 / 32;
-  float *hall = reinterpret_cast<float *>(lds_a);
+  constexpr int kHB = kTileGU / 32;  // h blocks per workgroup
+  const int p = lane & 15;
+  for (int it = tid >> 4; it < cnt * kHB; it += kPfThreads / 16) {
+    const int r = it / kHB, hb = it % kHB;
+    const size_t hrow = (size_t)rowbase + r;
+    const int fbg = n0 / 32 + hb;
+    uint32_t *dst = a.hp + (hrow * a.nb_f + fbg) * 32;
+    float share = prep_h_pair_rt(fdn, hs + r * kTileGU + 32 * hb, p, dst);
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const bool mine = active && (wave >> 2) == round;
-    float *hs = hall + (wave & 3) * kChunk * 32;
-    if (mine) {
-#pragma unroll
-      for (int mt = 0; mt < kMT; ++mt)
-        if (mt < nmt)
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              hs[(mt * 16 + 4 * kq + i) * 32 + 16 * nt + col] =
-                  silu(acc[mt][nt][0][i]) * acc[mt][nt][1][i];
-    }
-    __syncthreads();
-    if (mine) {
-      // 16 lanes per (row, block): four rows per pass of the wave
-      for (int r0 = 0; r0 < cnt; r0 += 4) {
-        const int r = r0 + (lane >> 4), p = lane & 15;
-        float share = 0.f;
-        const size_t hrow = (size_t)rowbase + r;
-        if (r < cnt) {
-          uint32_t *dst = a.hp + (hrow * a.nb_f + fbg) * 32;
-          share = prep_h_pair_rt(fdn, hs + r * 32, p, dst);
-        }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
-        if (r < cnt && p == 0) a.hnc[(size_t)fbg * (a.rows_max + 16) + hrow] = share;
-      }
-    }
-    __syncthreads();
+    for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
+    if (p == 0) a.hnc[(size_t)fbg * (a.rows_max + 16) + hrow] = share;
   }
 }
 
 template <int VX>
 __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PfArgs a) {
-  if ((int)blockIdx.y >= a.ntasks[0]) return;
-  const PfTask tk = a.tasks[blockIdx.y];
-  __shared__ __align__(16) uint32_t lds_a[kLdsAWords];
-  __shared__ __align__(16) float lds_nc[2 * 4 * kChunk];
-  __shared__ PfRows rows;
+  int t, slice;
+  if (!pf_work(a, a.f / kTileGU, &t, &slice)) return;
+  const PfTask tk = a.tasks[t];
+  __shared__ __align__(16) PfLds sm;
   const ExpertDesc ed = pf_desc(a, tk.expert);
   const int fmt = ed.fmt[0];
-  if (fmt == RFPX_FP2) pf_gateup_task<RFPX_FP2, VX>(a, tk, ed, lds_a, lds_nc, rows);
-  else if (fmt == RFPX_FP3) pf_gateup_task<RFPX_FP3, VX>(a, tk, ed, lds_a, lds_nc, rows);
-  else pf_gateup_task<RFPX_FP4, VX>(a, tk, ed, lds_a, lds_nc, rows);
+  if (fmt == RFPX_FP2) pf_gateup_task<RFPX_FP2, VX>(a, tk, ed, slice, sm);
+  else if (fmt == RFPX_FP3) pf_gateup_task<RFPX_FP3, VX>(a, tk, ed, slice, sm);
+  else pf_gateup_task<RFPX_FP4, VX>(a, tk, ed, slice, sm);
 }
 
 // ------------------------------------------------------------------- down
 
-// A workgroup covers kTileDN rows of the down matrix: four 16-row tiles per
+// A workgroup covers kTileDN rows of the down matrix: two 16-row tiles per
 // wave.
 template <int FMT>
-__device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed,
-                             uint32_t *lds_a, float *lds_nc, PfRows &rows) {
+__device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed, int slice,
+                             PfLds &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4, col = lane & 15;
   const int e = tk.expert, m0 = tk.m0, cnt = tk.rows;
   const int nmt = (cnt + 15) >> 4;
-  const bool active = (int)blockIdx.x * kTileDN + 64 * wave < a.d;  // see pf_gateup_task
-  const int row0 = active ? (int)blockIdx.x * kTileDN + 64 * wave : 0;
+  const int row0 = slice * kTileDN + 32 * wave;
   const int rowbase = a.offs[e] + m0;
   for (int r = tid; r < kChunk; r += kPfThreads) {
     const size_t row = (size_t)rowbase + (r < cnt ? r : 0);
-    rows.a_row[r] = (uint32_t)(row * a.nb_f * 128);
-    rows.nc_row[r] = (uint32_t)(row * 4);
+    sm.rows.a_row[r] = (uint32_t)(row * a.nb_f * 128);
+    sm.rows.nc_row[r] = (uint32_t)(row * 4);
   }
   __syncthreads();
   const __amdgpu_buffer_rsrc_t hpr =
       make_rsrc(a.hp, (uint32_t)((size_t)(a.rows_max + 16) * a.nb_f * 128));
   const __amdgpu_buffer_rsrc_t ncr =
       make_rsrc(a.hnc, (uint32_t)((size_t)a.nb_f * (a.rows_max + 16) * 4));
-  floatx4 acc[kMT][4][1];
+  floatx4 acc[kMT][2][1];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-  pf_gemm<FMT, 1, 4, 2, 2>(a, a.nb_f, nmt, hpr, 128, ncr, (a.rows_max + 16) * 4, rows, ed, 2,
-                           row0, a.nb_f, lds_a, lds_nc, acc);
+    for (int nt = 0; nt < 2; ++nt) acc[mt][nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
+  pf_gemm<FMT, 1, 2, 2, 2>(a, a.nb_f, nmt, hpr, 128, ncr, (a.rows_max + 16) * 4, sm.rows, ed, 2,
+                           row0, a.nb_f, sm.a, sm.nc, sm.b[wave], acc);
   const int *ltok = a.ltok + (size_t)e * a.T + m0;
   const int *lrank = a.lrank + (size_t)e * a.T + m0;
   const float *lw = a.lw + (size_t)e * a.T + m0;
@@ -703,27 +783,26 @@ __device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = mt * 16 + 4 * kq + i;
-        if (active && r < cnt) {
+        if (r < cnt) {
           const int t = ltok[r];
           float *o = a.out + ((size_t)t * (a.k + 1) + lrank[r]) * a.d + row0 + col;
           const float w = lw[r];
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) o[16 * nt] = w * acc[mt][nt][0][i];
+          for (int nt = 0; nt < 2; ++nt) o[16 * nt] = w * acc[mt][nt][0][i];
         }
       }
 }
 
 __global__ __launch_bounds__(kPfThreads) void k_pf_down(PfArgs a) {
-  if ((int)blockIdx.y >= a.ntasks[0]) return;
-  const PfTask tk = a.tasks[blockIdx.y];
-  __shared__ __align__(16) uint32_t lds_a[kLdsAWords];
-  __shared__ __align__(16) float lds_nc[2 * 4 * kChunk];
-  __shared__ PfRows rows;
+  int t, slice;
+  if (!pf_work(a, a.d / kTileDN, &t, &slice)) return;
+  const PfTask tk = a.tasks[t];
+  __shared__ __align__(16) PfLds sm;
   const ExpertDesc ed = pf_desc(a, tk.expert);
   const int fmt = ed.fmt[2];
-  if (fmt == RFPX_FP2) pf_down_task<RFPX_FP2>(a, tk, ed, lds_a, lds_nc, rows);
-  else if (fmt == RFPX_FP3) pf_down_task<RFPX_FP3>(a, tk, ed, lds_a, lds_nc, rows);
-  else pf_down_task<RFPX_FP4>(a, tk, ed, lds_a, lds_nc, rows);
+  if (fmt == RFPX_FP2) pf_down_task<RFPX_FP2>(a, tk, ed, slice, sm);
+  else if (fmt == RFPX_FP3) pf_down_task<RFPX_FP3>(a, tk, ed, slice, sm);
+  else pf_down_task<RFPX_FP4>(a, tk, ed, slice, sm);
 }
 
 // ---------------------------------------------------------------- combine
@@ -762,7 +841,7 @@ size_t prefill_layout(const moe_layer *L, int T, int xtype, void *args_out) {
   for (int e = 0; e <= L->n_experts; ++e) a.gu_fmts |= 1u << L->fmts[3 * e];
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
     if ((a.gu_fmts >> f) & 1u) a.fmt_slot[f] = nf++;
-  if (L->d % 64 || L->f % 64) return 0;
+  if (L->d % kTileDN || L->f % kTileGU) return 0;
   const size_t E1 = L->n_experts + 1;
   size_t off = 0;
   struct Item {
@@ -851,8 +930,9 @@ hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, f
   k_pf_group<<<a.E + 1, 256, 0, stream>>>(a);
   k_pf_plan<<<1, 1024, 0, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 ggu((a.f + kTileGU - 1) / kTileGU, a.max_tasks);
-  const dim3 gdn((a.d + kTileDN - 1) / kTileDN, a.max_tasks);
+  // workgroups: every task's slices, the tasks padded to a multiple of kXcds
+  const int tpad = (a.max_tasks + kXcds - 1) / kXcds * kXcds;
+  const int ggu = tpad * (a.f / kTileGU), gdn = tpad * (a.d / kTileDN);
   if (a.vx == 1) k_pf_gateup<1><<<ggu, kPfThreads, 0, stream>>>(a);
   else k_pf_gateup<2><<<ggu, kPfThreads, 0, stream>>>(a);
   k_pf_down<<<gdn, kPfThreads, 0, stream>>>(a);
