@@ -10,7 +10,7 @@
 //
 // The per-token result is the decode path's (moe_layer_forward with one
 // column per token); only the order of fp32 sums differs.  Launches:
-//   k_pf_scores  router scores S = X Wr^T, fp32 tiles through LDS.
+//   k_pf_scores  router scores S = X Wr^T, fp32 products on the matrix cores.
 //   k_pf_prep    prepared activations of every token and block for each
 //                gate/up format present (the decode path's pair words and
 //                accumulator starts, rfpx_impl.hpp).
@@ -86,55 +86,86 @@ struct PfArgs {
   float *out;          // [T][k+1][d]
 };
 
-__device__ __forceinline__ float load_x(const PfArgs &a, int t, int i) {
-  if (a.xtype == RFPX_X_BF16)
-    return bf16_bits_to_float(static_cast<const uint16_t *>(a.x)[(size_t)t * a.d + i]);
-  return static_cast<const float *>(a.x)[(size_t)t * a.d + i];
-}
-
 // ---------------------------------------------------------------- scores
 
-// S[t][e] = sum_i x[t][i] Wr[e][i]: 64 x 64 output tiles, k in steps of 32
-// through LDS, 4 x 4 outputs per thread, fp32 FMA.
-__global__ __launch_bounds__(256) void k_pf_scores(PfArgs a) {
-  __shared__ float xs[32][65];
-  __shared__ float ws[32][65];
-  const int t0 = blockIdx.y * 64, e0 = blockIdx.x * 64;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  float acc[4][4];
+// S[t][e] = sum_i x[t][i] Wr[e][i] on the matrix cores in fp32
+// (v_mfma_f32_16x16x4_f32: fp32 products, fp32 sums).  A wave owns 16
+// tokens x 32 experts (two 16 x 16 tiles); a workgroup of four waves 32
+// tokens x 64 experts, so its waves share each x and Wr fragment through
+// L1.  The order of the k terms inside a step of 32 is free: lane (kq, col)
+// takes k = 8 kq .. 8 kq + 7, i.e. 8 contiguous elements of its row, which
+// it loads in one or two 16-byte reads; the next step is loaded while the
+// current one runs.
+template <int XT>
+__device__ __forceinline__ void scores_load(const PfArgs &a, int t, int k, float *xv) {
+  if (XT == RFPX_X_BF16) {
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.x) +
+                                                      (size_t)t * a.d + k);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < a.d; k0 += 32) {
-    for (int i = tid; i < 64 * 32; i += 256) {
-      const int r = i >> 5, c = i & 31;
-      const int t = t0 + r, e = e0 + r;
-      xs[c][r] = t < a.T ? load_x(a, t, k0 + c) : 0.f;
-      ws[c][r] = e < a.E ? a.wr[(size_t)e * a.d + k0 + c] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      xv[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+      xv[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
     }
-    __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      float xv[4], wv[4];
+  } else {
+    const float *p = static_cast<const float *>(a.x) + (size_t)t * a.d + k;
+    const floatx4 v0 = *reinterpret_cast<const floatx4 *>(p);
+    const floatx4 v1 = *reinterpret_cast<const floatx4 *>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      xv[i] = v0[i];
+      xv[4 + i] = v1[i];
+    }
+  }
+}
+
+template <int XT>
+__global__ __launch_bounds__(256) void k_pf_scores(PfArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kq = lane >> 4, col = lane & 15;
+  const int t0 = blockIdx.y * 32 + 16 * (wave & 1), e0 = blockIdx.x * 64 + 32 * (wave >> 1);
+  const int t = min(t0 + col, a.T - 1);
+  const int er[2] = {min(e0 + col, a.E - 1), min(e0 + 16 + col, a.E - 1)};
+  floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  float xn[8], wn[2][8];
+  auto load = [&](int k0) {
+    const int k = k0 + 8 * kq;
+    scores_load<XT>(a, t, k, xn);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const float *p = a.wr + (size_t)er[n] * a.d + k;
+      const floatx4 v0 = *reinterpret_cast<const floatx4 *>(p);
+      const floatx4 v1 = *reinterpret_cast<const floatx4 *>(p + 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        xv[i] = xs[kk][ty * 4 + i];
-        wv[i] = ws[kk][tx * 4 + i];
+        wn[n][i] = v0[i];
+        wn[n][4 + i] = v1[i];
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
     }
-    __syncthreads();
+  };
+  load(0);
+  for (int k0 = 0; k0 < a.d; k0 += 32) {
+    float xc[8], wc[2][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xc[i] = xn[i];
+      wc[0][i] = wn[0][i];
+      wc[1][i] = wn[1][i];
+    }
+    if (k0 + 32 < a.d) load(k0 + 32);
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(xc[s], wc[n][s], acc[n], 0, 0, 0);
   }
+  // D[4 kq + i][col]: token t0 + 4 kq + i, expert e0 + 16 n + col
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = t0 + ty * 4 + i, e = e0 + tx * 4 + j;
-      if (t < a.T && e < a.E) a.scores[(size_t)t * a.E + e] = acc[i][j];
+    for (int i = 0; i < 4; ++i) {
+      const int tt = t0 + 4 * kq + i, e = e0 + 16 * n + col;
+      if (tt < a.T && e < a.E) a.scores[(size_t)tt * a.E + e] = acc[n][i];
     }
 }
 
@@ -920,7 +951,9 @@ hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, f
   a.wr = L->router_w;
   a.x = x;
   a.y = y;
-  k_pf_scores<<<dim3((a.E + 63) / 64, (T + 63) / 64), 256, 0, stream>>>(a);
+  const dim3 gsc((a.E + 63) / 64, (T + 31) / 32);
+  if (xtype == RFPX_X_BF16) k_pf_scores<RFPX_X_BF16><<<gsc, 256, 0, stream>>>(a);
+  else k_pf_scores<RFPX_X_F32><<<gsc, 256, 0, stream>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nf = __builtin_popcount(a.gu_fmts);
