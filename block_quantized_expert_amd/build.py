@@ -33,6 +33,12 @@ FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
+# Per-file additions.  The prefill products read every MFMA result at once
+# for the per-block scale; the VGPR form of the MFMA instructions saves the
+# copy out of the accumulation registers.
+EXTRA_FLAGS = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -40,7 +46,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        cmd = [cc, *FLAGS, "-c", src, "-o", obj]
+        cmd = [cc, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops" not in l)

@@ -485,9 +485,11 @@ constexpr int kBRegionBytes =
 // registers, to be stored to the other LDS buffer.  The B span of the
 // wave's rows is refilled from registers every SB/KC chunks, and the next
 // span is then requested.  NA = number of A terms per block (1, or 2 for
-// bf16 hi + lo), chained through the MFMA accumulator.
-template <int FMT, int NM, int NT, int NA, int KC>
-__device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
+// bf16 hi + lo), chained through the MFMA accumulator.  NMT = number of
+// 16-row tiles of A in use (a compile-time count, so that the products of a
+// block issue back to back).
+template <int FMT, int NM, int NT, int NA, int KC, int NMT>
+__device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
                                         __amdgpu_buffer_rsrc_t ar, uint32_t a_stride,
                                         __amdgpu_buffer_rsrc_t ncr, uint32_t nc_stride,
                                         const PfRows &rows, const ExpertDesc &ed, int mat0,
@@ -528,7 +530,7 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
   float rnc = 0.f;
   u32x4 rb[BS::NB];
 
-  auto issue_b = [&](int sp) {
+  auto issue_b = [&](int sp) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < BS::NB; ++q) {
       const int item = lane + 64 * q;
@@ -554,7 +556,7 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
                    : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto store_b = [&]() {
+  auto store_b = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < BS::NB; ++q) {
       const int item = lane + 64 * q;
@@ -563,7 +565,7 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
         *reinterpret_cast<u32x4 *>(lds_b + rr * BS::PITCH + 16 + 16 * p) = rb[q];
     }
   };
-  auto issue_a = [&](int c) {
+  auto issue_a = [&](int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int item = tid + kPfThreads * q;
@@ -580,7 +582,7 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
                                           ncr, (int)(rows.nc_row[r] + blk * nc_stride), 0, 0));
     }
   };
-  auto store_a = [&](int buf) {
+  auto store_a = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int item = tid + kPfThreads * q;
@@ -604,7 +606,7 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
     const int jb0 = (c % CPS) * KC;
     // shift of this span's scales within their first piece
     const uint32_t sadd = (BS::SB * BS::SBY) % 16 ? (uint32_t)((c / CPS) * BS::SB * BS::SBY) % 16 : 0u;
-#pragma unroll
+#pragma unroll 1
     for (int j = 0; j < KC; ++j) {
       if (c * KC + j < nblocks) {
         const uint32_t *la = lds_a + (buf * KC + j) * kChunk * AWP;
@@ -631,8 +633,8 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks, int nmt,
                                     : block_scale<FMT>(*reinterpret_cast<const uint16_t *>(sp));
           }
 #pragma unroll
-          for (int mt = 0; mt < kMT; ++mt) {
-            if (mt < nmt) {
+          for (int mt = 0; mt < NMT; ++mt) {
+            {
               bf16x8 av[NA];
 #pragma unroll
               for (int v = 0; v < NA; ++v)
@@ -710,7 +712,7 @@ __device__ __forceinline__ bool pf_work(const PfArgs &a, int nslices, int *task,
 // tile of both.  After the products the h tile goes through LDS, and the
 // workgroup prepares its kTileGU / 32 blocks of h for the down matrix.
 template <int FMT, int VX>
-__device__ void pf_gateup_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed, int slice,
+__device__ __forceinline__ void pf_gateup_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed, int slice,
                                PfLds &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4, col = lane & 15;
@@ -733,8 +735,17 @@ __device__ void pf_gateup_task(const PfArgs &a, const PfTask &tk, const ExpertDe
 #pragma unroll
     for (int m = 0; m < 2; ++m) acc[mt][0][m] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int row0 = n0 + 16 * wave;
-  pf_gemm<FMT, 2, 1, VX, (VX == 1 ? 4 : 2)>(a, a.nb_d, nmt, xpr, VX * 64, ncr, a.T * 4, sm.rows,
-                                             ed, 0, row0, a.nb_d, sm.a, sm.nc, sm.b[wave], acc);
+  constexpr int KC = VX == 1 ? 4 : 2;
+#define PF_GU(n)                                                                              \
+  pf_gemm<FMT, 2, 1, VX, KC, n>(a, a.nb_d, xpr, VX * 64, ncr, a.T * 4, sm.rows, ed, 0, row0, \
+                                a.nb_d, sm.a, sm.nc, sm.b[wave], acc)
+  switch (nmt) {
+    case 1: PF_GU(1); break;
+    case 2: PF_GU(2); break;
+    case 3: PF_GU(3); break;
+    default: PF_GU(4); break;
+  }
+#undef PF_GU
   // h tile [kChunk][kTileGU] in LDS, then h prepared for the down matrix:
   // 16 lanes per (row, block of 32)
   float *hs = reinterpret_cast<float *>(sm.a);
@@ -780,7 +791,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PfArgs a) {
 // A workgroup covers kTileDN rows of the down matrix: two 16-row tiles per
 // wave.
 template <int FMT>
-__device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed, int slice,
+__device__ __forceinline__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc &ed, int slice,
                              PfLds &sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kq = lane >> 4, col = lane & 15;
@@ -803,8 +814,16 @@ __device__ void pf_down_task(const PfArgs &a, const PfTask &tk, const ExpertDesc
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-  pf_gemm<FMT, 1, 2, 2, 2>(a, a.nb_f, nmt, hpr, 128, ncr, (a.rows_max + 16) * 4, sm.rows, ed, 2,
-                           row0, a.nb_f, sm.a, sm.nc, sm.b[wave], acc);
+#define PF_DN(n)                                                                             \
+  pf_gemm<FMT, 1, 2, 2, 2, n>(a, a.nb_f, hpr, 128, ncr, (a.rows_max + 16) * 4, sm.rows, ed, 2, \
+                              row0, a.nb_f, sm.a, sm.nc, sm.b[wave], acc)
+  switch (nmt) {
+    case 1: PF_DN(1); break;
+    case 2: PF_DN(2); break;
+    case 3: PF_DN(3); break;
+    default: PF_DN(4); break;
+  }
+#undef PF_DN
   const int *ltok = a.ltok + (size_t)e * a.T + m0;
   const int *lrank = a.lrank + (size_t)e * a.T + m0;
   const float *lw = a.lw + (size_t)e * a.T + m0;
