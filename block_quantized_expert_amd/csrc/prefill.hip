@@ -478,8 +478,22 @@ constexpr int kBRegionBytes =
                         : (BStage<RFPX_FP2>::PITCH > BStage<RFPX_FP4>::PITCH ? BStage<RFPX_FP2>::PITCH
                                                                              : BStage<RFPX_FP4>::PITCH));
 
+// A staging: two buffers of chunk x rows x (words of a block + 4 of padding).
+constexpr int kLdsAWords = 2 * 4 * kChunk * 20;
+
+// Blocks per chunk of the A staging for NMT tiles of 16 rows and NA terms:
+// as many as one LDS buffer holds (a power of two, at most the B span), so
+// that a task of few tokens passes fewer barriers.
+template <int FMT, int NA, int NMT>
+struct AChunk {
+  static constexpr int AWP = NA * 16 + 4;  // words per row and block (padded)
+  static constexpr int CAP = kLdsAWords / 2 / (16 * NMT * AWP);
+  static constexpr int KC0 = CAP >= 16 ? 16 : CAP >= 8 ? 8 : CAP >= 4 ? 4 : CAP >= 2 ? 2 : 1;
+  static constexpr int KC = KC0 < BStage<FMT>::SB ? KC0 : BStage<FMT>::SB;
+};
+
 // Output tile of a grouped product over nblocks blocks of 32: the task's
-// rows (at most kChunk) x NT 16-row tiles of NM matrices per wave.
+// rows (16 NMT, at most kChunk) x NT 16-row tiles of NM matrices per wave.
 // Software-pipelined in chunks of KC blocks: while chunk c is multiplied,
 // the A words (and accumulator starts) of chunk c+1 are in flight to
 // registers, to be stored to the other LDS buffer.  The B span of the
@@ -488,7 +502,7 @@ constexpr int kBRegionBytes =
 // bf16 hi + lo), chained through the MFMA accumulator.  NMT = number of
 // 16-row tiles of A in use (a compile-time count, so that the products of a
 // block issue back to back).
-template <int FMT, int NM, int NT, int NA, int KC, int NMT>
+template <int FMT, int NM, int NT, int NA, int NMT>
 __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
                                         __amdgpu_buffer_rsrc_t ar, uint32_t a_stride,
                                         __amdgpu_buffer_rsrc_t ncr, uint32_t nc_stride,
@@ -499,11 +513,14 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
   using BS = BStage<FMT>;
   static_assert(16 * NT * NM == kRowsPerWave, "a wave owns kRowsPerWave rows of B");
   static_assert(NM <= 2, "plane offsets are selected for at most two matrices");
+  constexpr int KC = AChunk<FMT, NA, NMT>::KC;
   static_assert(BS::SB % KC == 0, "a B span holds whole chunks");
   constexpr int AW = NA * 16, AWP = AW + 4, V4 = AW / 4;
-  constexpr int PPR = KC * V4;  // 16-byte pieces of one A row per chunk
-  static_assert(PPR == 16, "16 lanes per A row");
-  constexpr int NLD = kChunk * PPR / kPfThreads;
+  constexpr int ROWS = 16 * NMT;  // A rows staged
+  constexpr int PPR = KC * V4;    // 16-byte pieces of one A row per chunk (contiguous)
+  constexpr int NLD = ROWS * PPR / kPfThreads;
+  static_assert(NLD * kPfThreads == ROWS * PPR, "A loads must split evenly");
+  static_assert(KC * ROWS <= kPfThreads, "one accumulator start per thread");
   constexpr int CPS = BS::SB / KC;  // chunks per B span
   const int tid = threadIdx.x, lane = tid & 63, kq = lane >> 4, col = lane & 15;
   QuadDecode<FMT> qd;
@@ -575,8 +592,8 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
       ra[q] = __builtin_amdgcn_raw_buffer_load_b128(
           ar, (int)(rows.a_row[r] + blk * a_stride + 16 * w4), 0, 0);
     }
-    if (tid < KC * kChunk) {
-      const int r = tid % kChunk, j = tid / kChunk;
+    if (tid < KC * ROWS) {
+      const int r = tid % ROWS, j = tid / ROWS;
       const int blk = min(c * KC + j, nblocks - 1);
       rnc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                           ncr, (int)(rows.nc_row[r] + blk * nc_stride), 0, 0));
@@ -588,9 +605,9 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
       const int item = tid + kPfThreads * q;
       const int r = item / PPR, pc = item % PPR;
       const int j = pc / V4, w4 = pc % V4;
-      *reinterpret_cast<u32x4 *>(lds_a + ((buf * KC + j) * kChunk + r) * AWP + 4 * w4) = ra[q];
+      *reinterpret_cast<u32x4 *>(lds_a + ((buf * KC + j) * ROWS + r) * AWP + 4 * w4) = ra[q];
     }
-    if (tid < KC * kChunk) lds_nc[buf * KC * kChunk + tid] = rnc;
+    if (tid < KC * ROWS) lds_nc[buf * KC * ROWS + tid] = rnc;
   };
 
   issue_b(0);
@@ -609,8 +626,8 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
 #pragma unroll 1
     for (int j = 0; j < KC; ++j) {
       if (c * KC + j < nblocks) {
-        const uint32_t *la = lds_a + (buf * KC + j) * kChunk * AWP;
-        const float *ln = lds_nc + (buf * KC + j) * kChunk;
+        const uint32_t *la = lds_a + (buf * KC + j) * ROWS * AWP;
+        const float *ln = lds_nc + (buf * KC + j) * ROWS;
         const int jb = jb0 + j;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -670,8 +687,6 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
 // LDS of the prefill products: the A staging buffers (also the h tile of
 // the gate/up epilogue), the accumulator starts, the B regions of the
 // waves and the row table.
-constexpr int kLdsAWords = 2 * 4 * kChunk * 20;
-static_assert(2 * 2 * kChunk * 36 <= kLdsAWords, "down / fp32-x staging fits");
 static_assert(kChunk * kTileGU <= kLdsAWords, "h tile fits");
 
 struct PfLds {
@@ -735,10 +750,9 @@ __device__ __forceinline__ void pf_gateup_task(const PfArgs &a, const PfTask &tk
 #pragma unroll
     for (int m = 0; m < 2; ++m) acc[mt][0][m] = floatx4{0.f, 0.f, 0.f, 0.f};
   const int row0 = n0 + 16 * wave;
-  constexpr int KC = VX == 1 ? 4 : 2;
-#define PF_GU(n)                                                                              \
-  pf_gemm<FMT, 2, 1, VX, KC, n>(a, a.nb_d, xpr, VX * 64, ncr, a.T * 4, sm.rows, ed, 0, row0, \
-                                a.nb_d, sm.a, sm.nc, sm.b[wave], acc)
+#define PF_GU(n)                                                                          \
+  pf_gemm<FMT, 2, 1, VX, n>(a, a.nb_d, xpr, VX * 64, ncr, a.T * 4, sm.rows, ed, 0, row0, \
+                            a.nb_d, sm.a, sm.nc, sm.b[wave], acc)
   switch (nmt) {
     case 1: PF_GU(1); break;
     case 2: PF_GU(2); break;
@@ -814,9 +828,9 @@ __device__ __forceinline__ void pf_down_task(const PfArgs &a, const PfTask &tk, 
   for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[mt][nt][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-#define PF_DN(n)                                                                             \
-  pf_gemm<FMT, 1, 2, 2, 2, n>(a, a.nb_f, hpr, 128, ncr, (a.rows_max + 16) * 4, sm.rows, ed, 2, \
-                              row0, a.nb_f, sm.a, sm.nc, sm.b[wave], acc)
+#define PF_DN(n)                                                                          \
+  pf_gemm<FMT, 1, 2, 2, n>(a, a.nb_f, hpr, 128, ncr, (a.rows_max + 16) * 4, sm.rows, ed, 2, \
+                           row0, a.nb_f, sm.a, sm.nc, sm.b[wave], acc)
   switch (nmt) {
     case 1: PF_DN(1); break;
     case 2: PF_DN(2); break;
