@@ -138,6 +138,9 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
     }
   }
   p->g = q == 1 ? 1 : 2;
+  // with several columns the routing step costs more and every routed
+  // gate/up workgroup would repeat it: run it once before the experts
+  p->pre_route = q > 1;
   p->wmax = 8;  // waves per workgroup (a multiple of the column parts, 1 or 2)
   if (!pick_tile_gateup(p->geo_gu, p->gu_fmts, p->g, L->f, &p->rw_gu))
     return fail(RFPX_E_SHAPE, "f=%d: no gate/up tile for this format mix", L->f);

@@ -52,6 +52,7 @@ struct ExpArgs {
   float *y;
   int d, f, q, nb_d, nb_f;
   int rw_gu, rw_dn;
+  int pre_routed;  // the route table is complete before the launch
   Geo geo_gu[5], geo_dn[5];
 };
 
@@ -528,8 +529,9 @@ __device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, 
 }
 
 // Gate/up tile blockIdx.x of slot blockIdx.y.  Slot 0 is the shared expert
-// (every column, weight 1, no routing); routed slots run the routing step
-// in LDS first.
+// (every column, weight 1, no routing); routed slots read their entry of
+// the route table when it was built before the launch, else run the
+// routing step in LDS first.
 template <int G, int VX>
 __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
   const int slot = blockIdx.y;
@@ -544,15 +546,23 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     __syncthreads();
     sc.expert = a.rp.E;
     sc.ncols = a.q;
+    sc.cols = rs.cols[0];
+    sc.w = rs.w[0];
+  } else if (a.pre_routed) {
+    if (slot >= uniform(a.rt->nslots)) return;
+    sc.expert = uniform(a.rt->expert[slot]);
+    sc.ncols = uniform(a.rt->ncols[slot]);
+    sc.cols = a.rt->cols[slot];
+    sc.w = a.rt->w[slot];
   } else {
     route_wg(a.rp, &rs);
     if (slot >= uniform(rs.nslots)) return;
     if (blockIdx.x == 0) publish_route(rs, a.q, slot, slot == 1, a.rt);
     sc.expert = uniform(rs.expert[slot]);
     sc.ncols = uniform(rs.ncols[slot]);
+    sc.cols = rs.cols[slot];
+    sc.w = rs.w[slot];
   }
-  sc.cols = rs.cols[slot];
-  sc.w = rs.w[slot];
   gateup_wg<G, VX>(a, sc, slot, blockIdx.x, lds);
 }
 
@@ -729,6 +739,7 @@ ExpArgs make_args(const ForwardPlan &p) {
   }
   a.rw_gu = p.rw_gu;
   a.rw_dn = p.rw_dn;
+  a.pre_routed = p.pre_route ? 1 : 0;
   return a;
 }
 

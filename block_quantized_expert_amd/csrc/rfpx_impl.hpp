@@ -414,11 +414,13 @@ struct ForwardPlan {
   int wmax;                 // waves per workgroup
   int rw_gu, rw_dn;         // rows per workgroup tile
   bool route_only;
+  bool pre_route;           // the routing step runs once (k_topk) before the experts
   hipStream_t stream;
   void *const *events;      // optional: 4 hipEvent_t recorded around launches
 };
-// k_route: router scores and prepared activations; for route_only also
-// k_topk (ids and gating weights for moe_route_topk).
+// k_route: router scores and prepared activations; for route_only and
+// pre_route also k_topk (the route table; ids and gating weights for
+// moe_route_topk).
 hipError_t launch_route(const ForwardPlan &p);
 // Prefill (prefill.hip): workspace bytes for T tokens (0: unsupported
 // shape); with args_out, also the kernel arguments with workspace offsets.

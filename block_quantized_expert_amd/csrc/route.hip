@@ -14,9 +14,10 @@
 //   pair words in each gate/up format's decode order and per-block
 //   accumulator starts, rfpx_impl.hpp).  No cross-workgroup
 //   synchronization: the next launch reads both.
-// k_topk: one workgroup running the routing step (route_wg), for
-//   moe_route_topk.  In the layer forward the same step runs at the start of
-//   every routed gate/up workgroup instead.
+// k_topk: one workgroup running the routing step (route_wg) into the route
+//   table, for moe_route_topk and for layer steps of several columns.  In a
+//   one-column step the same step runs at the start of every routed gate/up
+//   workgroup instead (it is short there, and overlaps the shared expert).
 #include "rfpx_route.hpp"
 
 namespace rfpx {
@@ -105,11 +106,12 @@ __global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
   route_wg(a.rp, &s);
   const int tid = threadIdx.x;
   const int q = a.rp.q, k = a.rp.k;
-  for (int i = tid; i < q * k; i += blockDim.x) {
-    const int c = i / k, j = i % k;
-    a.ids_out[i] = s.ids[c][j];
-    a.w_out[i] = s.gw[c][j];
-  }
+  if (a.ids_out)
+    for (int i = tid; i < q * k; i += blockDim.x) {
+      const int c = i / k, j = i % k;
+      a.ids_out[i] = s.ids[c][j];
+      a.w_out[i] = s.gw[c][j];
+    }
   publish_route(s, q, -1, true, a.rt);  // the whole table
 }
 
@@ -136,7 +138,7 @@ hipError_t launch_route(const ForwardPlan &p) {
   const int n_prep_wg = (a.n_prep_items + kRouteThreads - 1) / kRouteThreads;
   k_route<<<a.n_router_wg + n_prep_wg, kRouteThreads, 0, p.stream>>>(a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !p.route_only) return e;
+  if (e != hipSuccess || !(p.route_only || p.pre_route)) return e;
   TopkArgs t{};
   t.rp = route_params(p);
   t.rt = reinterpret_cast<RouteTable *>(p.ws + p.wl.route);
