@@ -60,11 +60,11 @@ bool pow2_in(int v, int lo, int hi) {
 // Rows per workgroup tile.  A unit is R rows (rpi rows per wave step) of one
 // column part; R depends on the format and the pass width (unit_rows_for).
 // Gate/up tiles hold whole 32-row blocks of h (the down matrix's blocks).
-bool pick_tile_gateup(const Geo *geo, unsigned fmts, int g, int rows, int *rw) {
-  int t = 32;
+bool pick_tile_gateup(const Geo *geo, unsigned fmts, int g, int rows, int min_rows, int *rw) {
+  int t = 32 > min_rows ? 32 : min_rows;
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
     if ((fmts >> f) & 1u) {
-      const int unit = geo[f].rpi * unit_rows_for(f, g);
+      const int unit = geo[f].rpi * unit_rows_gu(f, g);
       t = t > unit ? t : unit;
     }
   if (t > rows || rows % t) return false;
@@ -74,8 +74,9 @@ bool pick_tile_gateup(const Geo *geo, unsigned fmts, int g, int rows, int *rw) {
 
 // Down tiles: about 512 workgroups over the d rows (two per compute unit),
 // and at least one unit of every present format.
-bool pick_tile_down(const Geo *geo, unsigned fmts, int g, int rows, int *rw) {
+bool pick_tile_down(const Geo *geo, unsigned fmts, int g, int rows, int min_rows, int *rw) {
   int t = rows / 512 > 1 ? rows / 512 : 1;
+  t = t > min_rows ? t : min_rows;
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
     if ((fmts >> f) & 1u) {
       const int unit = geo[f].rpi * unit_rows_for(f, g);
@@ -141,10 +142,18 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   // with several columns the routing step costs more and every routed
   // gate/up workgroup would repeat it: run it once before the experts
   p->pre_route = q > 1;
-  p->wmax = 8;  // waves per workgroup (a multiple of the column parts, 1 or 2)
-  if (!pick_tile_gateup(p->geo_gu, p->gu_fmts, p->g, L->f, &p->rw_gu))
+  // waves per down workgroup (a multiple of the column parts, 1 or 2)
+  p->wmax = q == 1 ? 8 : kDnWavesQn;
+  // gate/up workgroups: waves and the smallest tile; a wave streams
+  // rw_gu / (4 rpi) * parts / waves units with the next one in flight
+  p->wgu = q == 1 ? kGuWavesQ1 : kGuWavesQn;
+  const int gu_min = q == 1 ? kGuRowsQ1 : kGuRowsQn;
+  if (!pick_tile_gateup(p->geo_gu, p->gu_fmts, p->g, L->f, gu_min < L->f ? gu_min : L->f,
+                        &p->rw_gu))
     return fail(RFPX_E_SHAPE, "f=%d: no gate/up tile for this format mix", L->f);
-  if (!pick_tile_down(p->geo_dn, p->down_fmts, p->g, L->d, &p->rw_dn))
+  const int dn_min = q == 1 ? 1 : kDnRowsQn;
+  if (!pick_tile_down(p->geo_dn, p->down_fmts, p->g, L->d, dn_min < L->d ? dn_min : L->d,
+                      &p->rw_dn))
     return fail(RFPX_E_SHAPE, "d=%d: no down tile for this format mix", L->d);
   if ((size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024)
     return fail(RFPX_E_SHAPE, "f=%d, q=%d: down tile of %d rows needs too much LDS", L->f, q,

@@ -381,12 +381,86 @@ __device__ __forceinline__ UnitPos unit_pos(int u, int parts, int r, int rpi) {
 
 // ------------------------------------------------------------ gate / up
 
+// Part sums of one computed unit to LDS: gup[m][part][column][row].
+template <int FMT, int GP, int R>
+__device__ __forceinline__ void gateup_reduce(const float (&tot)[R][2][GP], const Geo &geo,
+                                              const UnitPos &up, int c0, int P, int q, int rw,
+                                              float *gup) {
+  const int lane = threadIdx.x & 63;
+  const int rg = lane / geo.lpr, li = lane % geo.lpr;
+  if (geo.lpr == 64) {  // one row per wave step: reduce all values at once
+    constexpr int N = R * 2 * GP;
+    float flat[N];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int g = 0; g < GP; ++g) flat[(i * 2 + m) * GP + g] = tot[i][m][g];
+    const float v = multi_sum<N>(flat, lane);
+    if (ms_writer<N>(lane)) {
+      const int n = ms_index<N>(lane);
+      const int i = n / (2 * GP), m = (n / GP) % 2, g = n % GP;
+      gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + i] = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+          const float v = group_sum(tot[i][m][g], geo.lpr);
+          if (li == 0)
+            gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i] = v;
+        }
+  }
+}
+
+// One pass of one column over the wave's units u = wave, wave + waves, ...
+// (all in part wave % P, since waves is a multiple of P), for one-column
+// steps: a tile gives each wave about one unit, so all of a unit's loads go
+// out at once and there is no second register set (whose registers would
+// halve the waves per SIMD).
+template <int FMT, int VX, int R>
+__device__ __forceinline__ void gateup_pass1(const ExpArgs &a, const SlotCols &sc, int c0,
+                                             const Geo &geo, int units, int wave, int waves,
+                                             int tile, const MatPtr (&mats)[2], uint32_t cpitch,
+                                             uint32_t spitch, float *gup) {
+  using F = Fmt<FMT>;
+  const int lane = threadIdx.x & 63;
+  const int rg = lane / geo.lpr, li = lane % geo.lpr;
+  const int P = geo.tpl, rw = a.rw_gu, q = a.q;
+  const int colidx[1] = {sc.col(c0)};
+  int u = wave;
+  UnitPos up = unit_pos(u, P, R, geo.rpi);
+  const int ch = li + geo.lpr * up.part;
+  const uint32_t coff = (uint32_t)(rg * cpitch + ch * F::CBYTES);
+  const uint32_t soff = (uint32_t)(rg * spitch + ch * F::SBYTES);
+  uint32_t cw[R][2][F::CW], sw[R][2];
+  unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cw, sw);
+  uint32_t xr[1][F::CB][VX][16];
+  float ncr[1][F::CB];
+  load_prepared_x<FMT, 1, VX>(a, colidx, ch, xr, ncr);
+  const uint32_t one = one_one_vgpr();
+  while (true) {
+    float tot[R][2][1];
+    unit_compute<FMT, 1, VX, 2, R>(cw, sw, xr, ncr, one, tot);
+    gateup_reduce<FMT, 1, R>(tot, geo, up, c0, P, q, rw, gup);
+    u += waves;
+    if (u >= units) break;
+    up = unit_pos(u, P, R, geo.rpi);
+    unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cw, sw);
+  }
+}
+
 // One pass of GP columns (c0 .. c0+GP-1 of the slot) over the wave's units
 // u = wave, wave + waves, ... (all in part wave % P, since waves is a
-// multiple of P): the first unit's weight loads go out, then the prepared
-// activations of the wave's chunk are loaded (once for all its units), then
-// each unit is decoded, reduced across lanes, and written as part sums to
-// LDS.
+// multiple of P), for steps of several columns.  The prepared activations
+// of the wave's chunk are loaded once for all its units; the code and scale
+// loads of the next unit are in flight while a unit is decoded (two
+// register sets, used in turn), so a wave streams its units without waiting
+// a full memory latency for each.
 template <int FMT, int GP, int VX, int R>
 __device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc, int c0,
                                             const Geo &geo, int units, int wave, int waves,
@@ -404,46 +478,41 @@ __device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc
   const int ch = li + geo.lpr * up.part;
   const uint32_t coff = (uint32_t)(rg * cpitch + ch * F::CBYTES);
   const uint32_t soff = (uint32_t)(rg * spitch + ch * F::SBYTES);
-  uint32_t cw[R][2][F::CW], sw[R][2];
-  unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cw, sw);
+  uint32_t cwa[R][2][F::CW], swa[R][2], cwb[R][2][F::CW], swb[R][2];
+  unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cwa, swa);
   uint32_t xr[GP][F::CB][VX][16];
   float ncr[GP][F::CB];
   load_prepared_x<FMT, GP, VX>(a, colidx, ch, xr, ncr);
   const uint32_t one = one_one_vgpr();
   while (true) {
-    float tot[R][2][GP];
-    unit_compute<FMT, GP, VX, 2, R>(cw, sw, xr, ncr, one, tot);
-    if (geo.lpr == 64) {  // one row per wave step: reduce all values at once
-      constexpr int N = R * 2 * GP;
-      float flat[N];
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int g = 0; g < GP; ++g) flat[(i * 2 + m) * GP + g] = tot[i][m][g];
-      const float v = multi_sum<N>(flat, lane);
-      if (ms_writer<N>(lane)) {
-        const int n = ms_index<N>(lane);
-        const int i = n / (2 * GP), m = (n / GP) % 2, g = n % GP;
-        gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + i] = v;
+    {
+      const int un = u + waves;
+      UnitPos upn{};
+      if (un < units) {
+        upn = unit_pos(un, P, R, geo.rpi);
+        unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + upn.rloc_u, geo.rpi, coff, soff, cwb, swb);
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < R; ++i)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int g = 0; g < GP; ++g) {
-            const float v = group_sum(tot[i][m][g], geo.lpr);
-            if (li == 0)
-              gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i] = v;
-          }
+      float tot[R][2][GP];
+      unit_compute<FMT, GP, VX, 2, R>(cwa, swa, xr, ncr, one, tot);
+      gateup_reduce<FMT, GP, R>(tot, geo, up, c0, P, q, rw, gup);
+      u = un;
+      up = upn;
+      if (u >= units) break;
     }
-    u += waves;
-    if (u >= units) break;
-    up = unit_pos(u, P, R, geo.rpi);
-    unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cw, sw);
+    {
+      const int un = u + waves;
+      UnitPos upn{};
+      if (un < units) {
+        upn = unit_pos(un, P, R, geo.rpi);
+        unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + upn.rloc_u, geo.rpi, coff, soff, cwa, swa);
+      }
+      float tot[R][2][GP];
+      unit_compute<FMT, GP, VX, 2, R>(cwb, swb, xr, ncr, one, tot);
+      gateup_reduce<FMT, GP, R>(tot, geo, up, c0, P, q, rw, gup);
+      u = un;
+      up = upn;
+      if (u >= units) break;
+    }
   }
 }
 
@@ -453,8 +522,9 @@ template <int FMT, int G, int VX>
 __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc,
                                             const ExpertDesc &ed, int tile, float *hs,
                                             float *gup) {
-  constexpr int R = unit_rows_for(FMT, G);
+  constexpr int R = unit_rows_gu(FMT, G);
   const Geo geo = a.geo_gu[FMT];
+  static_assert(G == 2 || R == unit_rows_for(FMT, 1), "one-column steps keep their unit rows");
   const uint32_t cpitch = (uint32_t)(a.d / 32) * code_bytes(FMT);
   const uint32_t spitch = (uint32_t)(a.d / 32) * scale_bytes(FMT);
   const MatPtr mats[2] = {
@@ -470,7 +540,9 @@ __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc
   for (int c0 = 0; c0 < sc.ncols; c0 += GD) {
     const int gc = (GD == 2 && sc.ncols - c0 >= 2) ? 2 : 1;
     if (wave < units) {
-      if constexpr (GD == 2) {
+      if constexpr (G == 1) {
+        gateup_pass1<FMT, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
+      } else if constexpr (GD == 2) {
         if (gc == 2)
           gateup_pass<FMT, 2, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
         else
@@ -625,6 +697,126 @@ __device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, 
   }
 }
 
+// Weighted row results of one computed down unit into the wave's
+// accumulator rows accw[column][row] (LDS, one writer lane per entry).  The
+// columns and weights come as separate scalars: a two-entry array indexed
+// by a lane value would be placed in scratch memory.
+template <int GP, int R>
+__device__ __forceinline__ void down_reduce(const float (&to)[R][1][GP], const Geo &geo,
+                                            const UnitPos &up, int rw, int col0, int col1,
+                                            float wgt0, float wgt1, float *accw) {
+  const int lane = threadIdx.x & 63;
+  const int rg = lane / geo.lpr, li = lane % geo.lpr;
+  if (geo.lpr == 64) {
+    constexpr int N = R * GP;
+    float flat[N];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int g = 0; g < GP; ++g) flat[i * GP + g] = to[i][0][g];
+    const float v = multi_sum<N>(flat, lane);
+    if (ms_writer<N>(lane)) {
+      const int n = ms_index<N>(lane);
+      const int i = n / GP, g = n % GP;
+      const int cg = (GP == 2 && g) ? col1 : col0;
+      const float wg = (GP == 2 && g) ? wgt1 : wgt0;
+      accw[cg * rw + up.rloc_u + i] += wg * v;
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float v = group_sum(to[i][0][g], geo.lpr);
+        if (li == 0) accw[(g ? col1 : col0) * rw + up.rloc_u + rg + geo.rpi * i] += (g ? wgt1 : wgt0) * v;
+      }
+  }
+}
+
+// Units [u0, u1) of one slot's down matrix for GP compact columns c0..,
+// all in column part 0: the wave loads the slot's prepared h of its chunk
+// once and streams the units with the next unit's code and scale loads in
+// flight while one is decoded (two register sets, used in turn).
+template <int FMT, int GP, int R>
+__device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, int slot, int c0,
+                                         const Geo &geo, int u0, int u1, int r0,
+                                         const MatPtr (&mats)[1], uint32_t cpitch,
+                                         uint32_t spitch, float *accw) {
+  using F = Fmt<FMT>;
+  const int lane = threadIdx.x & 63;
+  const int rg = lane / geo.lpr, li = lane % geo.lpr;
+  const int ch = li;
+  const uint32_t coff = (uint32_t)(rg * cpitch + ch * F::CBYTES);
+  const uint32_t soff = (uint32_t)(rg * spitch + ch * F::SBYTES);
+  const int P = geo.tpl, rw = a.rw_dn;
+  uint32_t cwa[R][1][F::CW], swa[R][1], cwb[R][1][F::CW], swb[R][1];
+  int u = u0;
+  UnitPos up = unit_pos(u, P, R, geo.rpi);
+  unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + up.rloc_u, geo.rpi, coff, soff, cwa, swa);
+  const uint32_t *hps = a.hp + (size_t)slot * a.q * a.nb_f * 32;
+  const float *hncs = a.hnc + (size_t)slot * a.q * a.nb_f;
+  uint32_t xr[GP][F::CB][2][16];
+  float ncr[GP][F::CB];
+  load_prepared_h<FMT, GP>(hps, hncs, a.nb_f, c0, ch, xr, ncr);
+  const int col0 = sc.col(c0), col1 = GP == 2 ? sc.col(c0 + GP - 1) : col0;
+  const float wgt0 = sc.weight(c0), wgt1 = GP == 2 ? sc.weight(c0 + GP - 1) : wgt0;
+  const uint32_t one = one_one_vgpr();
+  while (true) {
+    {
+      const int un = u + 1;
+      UnitPos upn{};
+      if (un < u1) {
+        upn = unit_pos(un, P, R, geo.rpi);
+        unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + upn.rloc_u, geo.rpi, coff, soff, cwb, swb);
+      }
+      float to[R][1][GP];
+      unit_compute<FMT, GP, 2, 1, R>(cwa, swa, xr, ncr, one, to);
+      down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
+      u = un;
+      up = upn;
+      if (u >= u1) break;
+    }
+    {
+      const int un = u + 1;
+      UnitPos upn{};
+      if (un < u1) {
+        upn = unit_pos(un, P, R, geo.rpi);
+        unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + upn.rloc_u, geo.rpi, coff, soff, cwa, swa);
+      }
+      float to[R][1][GP];
+      unit_compute<FMT, GP, 2, 1, R>(cwb, swb, xr, ncr, one, to);
+      down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
+      u = un;
+      up = upn;
+      if (u >= u1) break;
+    }
+  }
+}
+
+// Units [u0, u1) of one slot for every column of the slot, in passes of
+// up to G columns (FP2 down matrices one column per pass: their chunks hold
+// two blocks, so two-column passes would need 128 registers of h).
+template <int FMT, int G>
+__device__ __forceinline__ void down_slot_run(const ExpArgs &a, const SlotCols &sc, int slot,
+                                              const ExpertDesc &ed, int r0, int u0, int u1,
+                                              float *accw) {
+  constexpr int R = unit_rows_for(FMT, G);
+  const Geo geo = a.geo_dn[FMT];
+  const uint32_t cpitch = (uint32_t)(a.f / 32) * code_bytes(FMT);
+  const uint32_t spitch = (uint32_t)(a.f / 32) * scale_bytes(FMT);
+  const MatPtr mats[1] = {
+      {make_rsrc(a.image + ed.codes[2], a.d * cpitch), make_rsrc(a.image + ed.scales[2], a.d * spitch)}};
+  constexpr int GD = FMT == RFPX_FP2 ? 1 : G;
+  for (int c0 = 0; c0 < sc.ncols; c0 += GD) {
+    if constexpr (GD == 2) {
+      if (sc.ncols - c0 >= 2) down_run<FMT, 2, R>(a, sc, slot, c0, geo, u0, u1, r0, mats, cpitch, spitch, accw);
+      else down_run<FMT, 1, R>(a, sc, slot, c0, geo, u0, u1, r0, mats, cpitch, spitch, accw);
+    } else {
+      down_run<FMT, 1, R>(a, sc, slot, c0, geo, u0, u1, r0, mats, cpitch, spitch, accw);
+    }
+  }
+}
+
 // The units of one slot that fall to this wave: units are dealt to the
 // waves round-robin in slot order (`item` counts the units dealt so far).
 template <int FMT, int G>
@@ -694,8 +886,44 @@ __global__ __launch_bounds__(512) void k_down(ExpArgs a) {
   __syncthreads();
   const int r0 = blockIdx.x * rw;
   float *accw = acc + wave * q * rw;
+  // Steps of several columns: the units of all slots in slot order, cut
+  // into one contiguous run per wave (a run keeps a slot's h in registers
+  // across its units); needs every down format in one column part.
+  // (units per slot by format, selected: a kernel-argument array indexed
+  // at run time would be copied to scratch memory)
+  const bool runs = G == 2 && a.geo_dn[RFPX_FP2].tpl <= 1 && a.geo_dn[RFPX_FP3].tpl <= 1 &&
+                    a.geo_dn[RFPX_FP4].tpl <= 1;
+  const int ups2 = rw / (unit_rows_for(RFPX_FP2, G) * a.geo_dn[RFPX_FP2].rpi);
+  const int ups3 = rw / (unit_rows_for(RFPX_FP3, G) * a.geo_dn[RFPX_FP3].rpi);
+  const int ups4 = rw / (unit_rows_for(RFPX_FP4, G) * a.geo_dn[RFPX_FP4].rpi);
+  auto slot_units = [&](int fmt) { return fmt == RFPX_FP2 ? ups2 : fmt == RFPX_FP3 ? ups3 : ups4; };
+  if (runs) {
+    int total = 0;
+    for (int s = 0; s < nslots; ++s) total += slot_units(uniform(t_fmt[s]));
+    const int lo = total * wave / waves, hi = total * (wave + 1) / waves;
+    int start = 0;
+    for (int s = 0; s < nslots && start < hi; ++s) {
+      const int fmt = uniform(t_fmt[s]);
+      const int ups = slot_units(fmt);
+      const int u0 = lo > start ? lo - start : 0, u1 = hi < start + ups ? hi - start : ups;
+      if (u0 < u1) {
+        SlotCols sc;
+        sc.expert = -1;
+        sc.ncols = uniform(t_ncols[s]);
+        sc.cols = t_cols[s];
+        sc.w = t_w[s];
+        ExpertDesc ed{};
+        ed.codes[2] = uniform64(t_codes[s]);
+        ed.scales[2] = uniform64(t_scales[s]);
+        if (fmt == RFPX_FP2) down_slot_run<RFPX_FP2, G>(a, sc, s, ed, r0, u0, u1, accw);
+        else if (fmt == RFPX_FP3) down_slot_run<RFPX_FP3, G>(a, sc, s, ed, r0, u0, u1, accw);
+        else down_slot_run<RFPX_FP4, G>(a, sc, s, ed, r0, u0, u1, accw);
+      }
+      start += ups;
+    }
+  }
   int item = 0;
-  for (int s = 0; s < nslots; ++s) {
+  for (int s = 0; s < nslots && !runs; ++s) {
     SlotCols sc;
     sc.expert = -1;  // not needed: the down entry is in LDS
     sc.ncols = uniform(t_ncols[s]);
@@ -750,15 +978,15 @@ hipError_t launch_experts(const ForwardPlan &p) {
   const dim3 ggu(p.f / p.rw_gu, p.wl.max_slots), gdn(p.d / p.rw_dn);
   const size_t lds_gu = (size_t)5 * p.q * p.rw_gu * sizeof(float);        // hs + gup
   const size_t lds_dn = (size_t)p.wmax * p.q * p.rw_dn * sizeof(float);   // acc
-  const unsigned nt = 64 * p.wmax;
+  const unsigned nt = 64 * p.wmax, ntg = 64 * p.wgu;
   const bool bf = p.xtype == RFPX_X_BF16;
   hipEvent_t *ev = (hipEvent_t *)p.events;
   if (p.g == 1) {
-    if (bf) k_gateup<1, 1><<<ggu, nt, lds_gu, p.stream>>>(a);
-    else k_gateup<1, 2><<<ggu, nt, lds_gu, p.stream>>>(a);
+    if (bf) k_gateup<1, 1><<<ggu, ntg, lds_gu, p.stream>>>(a);
+    else k_gateup<1, 2><<<ggu, ntg, lds_gu, p.stream>>>(a);
   } else {
-    if (bf) k_gateup<2, 1><<<ggu, nt, lds_gu, p.stream>>>(a);
-    else k_gateup<2, 2><<<ggu, nt, lds_gu, p.stream>>>(a);
+    if (bf) k_gateup<2, 1><<<ggu, ntg, lds_gu, p.stream>>>(a);
+    else k_gateup<2, 2><<<ggu, ntg, lds_gu, p.stream>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && ev) e = hipEventRecord(ev[2], p.stream);

@@ -150,6 +150,35 @@ struct WsLayout {
 __host__ __device__ constexpr int unit_rows_for(int fmt, int g) {
   return (g == 1 && fmt != RFPX_FP2) ? 8 : 4;
 }
+// Gate/up workgroup shape by step width (waves; smallest tile in rows).
+#ifndef RFPX_GU_WAVES_Q1
+#define RFPX_GU_WAVES_Q1 8
+#endif
+#ifndef RFPX_GU_ROWS_Q1
+#define RFPX_GU_ROWS_Q1 32
+#endif
+#ifndef RFPX_GU_WAVES_QN
+#define RFPX_GU_WAVES_QN 4
+#endif
+#ifndef RFPX_GU_ROWS_QN
+#define RFPX_GU_ROWS_QN 32
+#endif
+#ifndef RFPX_DN_WAVES_QN
+#define RFPX_DN_WAVES_QN 8
+#endif
+#ifndef RFPX_DN_ROWS_QN
+#define RFPX_DN_ROWS_QN 16
+#endif
+constexpr int kGuWavesQ1 = RFPX_GU_WAVES_Q1, kGuRowsQ1 = RFPX_GU_ROWS_Q1;
+constexpr int kGuWavesQn = RFPX_GU_WAVES_QN, kGuRowsQn = RFPX_GU_ROWS_QN;
+constexpr int kDnWavesQn = RFPX_DN_WAVES_QN, kDnRowsQn = RFPX_DN_ROWS_QN;
+
+// Gate/up units of steps of several columns are 4 rows: a wave keeps the
+// next unit's loads in flight while it decodes one (two register sets);
+// one-column steps keep single sets of unit_rows_for rows.
+__host__ __device__ constexpr int unit_rows_gu(int fmt, int g) {
+  return g == 1 ? unit_rows_for(fmt, 1) : 4;
+}
 
 // ------------------------------------------------------------ device side
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
@@ -411,7 +440,8 @@ struct ForwardPlan {
   unsigned down_fmts;       // bit f set: down format f is present
   Geo geo_gu[5], geo_dn[5];  // indexed by format
   int g;                    // columns per pass of the expert kernels (1, 2)
-  int wmax;                 // waves per workgroup
+  int wmax;                 // waves per down workgroup
+  int wgu;                  // waves per gate/up workgroup
   int rw_gu, rw_dn;         // rows per workgroup tile
   bool route_only;
   bool pre_route;           // the routing step runs once (k_topk) before the experts
