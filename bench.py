@@ -377,8 +377,11 @@ def main() -> int:
             "router_bytes_per_step": cfg.E * cfg.d * 4,
         },
         "kernels_us": {
-            "k_route (router scores + prepared activations)": 1e3 * float(np.mean(k_route)),
-            "k_gateup (routing + gate/up of the shared and routed experts)": gu_us,
+            ("k_route (router scores + prepared activations)" if cfg.q == 1 else
+             "k_route + k_topk (router scores, prepared activations, route table)"):
+                1e3 * float(np.mean(k_route)),
+            ("k_gateup (routing + gate/up of the shared and routed experts)" if cfg.q == 1 else
+             "k_gateup (gate/up of the shared and routed experts)"): gu_us,
             "k_down (down of all slots + combine)": 1e3 * float(np.mean(k_dn)),
             "step_with_events": total_ev_ms * 1e3 / args.steps,
         },

@@ -621,11 +621,19 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     sc.cols = rs.cols[0];
     sc.w = rs.w[0];
   } else if (a.pre_routed) {
+    // the slot's entry of the route table, copied to LDS (the column list
+    // is then read through an LDS pointer on every path; a pointer that may
+    // be either LDS or global memory makes every read a slower flat access)
     if (slot >= uniform(a.rt->nslots)) return;
     sc.expert = uniform(a.rt->expert[slot]);
     sc.ncols = uniform(a.rt->ncols[slot]);
-    sc.cols = a.rt->cols[slot];
-    sc.w = a.rt->w[slot];
+    if (threadIdx.x < kQMax) {
+      rs.cols[slot][threadIdx.x] = a.rt->cols[slot][threadIdx.x];
+      rs.w[slot][threadIdx.x] = a.rt->w[slot][threadIdx.x];
+    }
+    __syncthreads();
+    sc.cols = rs.cols[slot];
+    sc.w = rs.w[slot];
   } else {
     route_wg(a.rp, &rs);
     if (slot >= uniform(rs.nslots)) return;
