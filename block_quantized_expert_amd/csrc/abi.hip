@@ -143,7 +143,7 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   // gate/up workgroup would repeat it: run it once before the experts
   p->pre_route = q > 1;
   // waves per down workgroup (a multiple of the column parts, 1 or 2)
-  p->wmax = q == 1 ? 8 : kDnWavesQn;
+  p->wmax = q == 1 ? kDnWavesQ1 : kDnWavesQn;
   // gate/up workgroups: waves and the smallest tile; a wave streams
   // rw_gu / (4 rpi) * parts / waves units with the next one in flight
   p->wgu = q == 1 ? kGuWavesQ1 : kGuWavesQn;
@@ -151,7 +151,7 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   if (!pick_tile_gateup(p->geo_gu, p->gu_fmts, p->g, L->f, gu_min < L->f ? gu_min : L->f,
                         &p->rw_gu))
     return fail(RFPX_E_SHAPE, "f=%d: no gate/up tile for this format mix", L->f);
-  const int dn_min = q == 1 ? 1 : kDnRowsQn;
+  const int dn_min = q == 1 ? kDnRowsQ1 : kDnRowsQn;
   if (!pick_tile_down(p->geo_dn, p->down_fmts, p->g, L->d, dn_min < L->d ? dn_min : L->d,
                       &p->rw_dn))
     return fail(RFPX_E_SHAPE, "d=%d: no down tile for this format mix", L->d);

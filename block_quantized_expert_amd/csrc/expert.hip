@@ -272,98 +272,6 @@ __device__ __forceinline__ float group_sum(float v, int lpr) {
   return v;
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-
-// One halving step of a multi-value reduction: lanes paired by the DPP
-// involution CTRL (which flips lane bit B, and maybe lower bits that no
-// earlier step has used) split each pair of values between them: the lane
-// with bit B clear keeps the even value plus its partner's even value, the
-// other the odd one.
-template <int CTRL, int B, int N>
-__device__ __forceinline__ void ms_step(const float (&v)[N], float (&w)[N / 2], int lane) {
-  const bool odd = (lane >> B) & 1;
-#pragma unroll
-  for (int i = 0; i < N / 2; ++i) {
-    const float keep = odd ? v[2 * i + 1] : v[2 * i];
-    const float send = odd ? v[2 * i] : v[2 * i + 1];
-    w[i] = keep + dpp_f<CTRL>(send);
-  }
-}
-
-// Sums of N values (N = 2, 4, 8, 16) over the 64 lanes of a wave, all at
-// once: log2(N) halving steps over lane bits 3, 2, 1, 0 (row_mirror,
-// row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2], in that order,
-// so that each step's partner agrees on every bit used before), plain DPP
-// sums over the remaining bits of a 16-lane row, and lane shuffles across
-// the four rows.  Lane l then holds the total of value ms_index<N>(l); the
-// lanes ms_writer<N>(l) hold each value once.  About 3N + 8 VALU ops
-// instead of 14 per value.
-template <int N>
-__device__ __forceinline__ float multi_sum(const float (&v)[N], int lane) {
-  float r;
-  if constexpr (N == 1) {
-    r = v[0];
-    r += dpp_f<0x140>(r);
-    r += dpp_f<0x141>(r);
-    r += dpp_f<0x4E>(r);
-    r += dpp_f<0xB1>(r);
-  } else {
-    float a[N / 2];
-    ms_step<0x140, 3, N>(v, a, lane);
-    if constexpr (N == 2) {
-      r = a[0];
-      r += dpp_f<0x141>(r);
-      r += dpp_f<0x4E>(r);
-      r += dpp_f<0xB1>(r);
-    } else {
-      float b[N / 4];
-      ms_step<0x141, 2, N / 2>(a, b, lane);
-      if constexpr (N == 4) {
-        r = b[0];
-        r += dpp_f<0x4E>(r);
-        r += dpp_f<0xB1>(r);
-      } else {
-        float c[N / 8];
-        ms_step<0x4E, 1, N / 4>(b, c, lane);
-        if constexpr (N == 8) {
-          r = c[0] + dpp_f<0xB1>(c[0]);
-        } else {
-          static_assert(N == 16, "multi_sum: N must be 1, 2, 4, 8 or 16");
-          float d[1];
-          ms_step<0xB1, 0, 2>(c, d, lane);
-          r = d[0];
-        }
-      }
-    }
-  }
-  r += __shfl_xor(r, 16, 64);
-  r += __shfl_xor(r, 32, 64);
-  return r;
-}
-
-template <int N>
-__device__ __forceinline__ int ms_index(int lane) {
-  const int b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1, b1 = (lane >> 1) & 1, b0 = lane & 1;
-  if (N == 1) return 0;
-  if (N == 2) return b3;
-  if (N == 4) return b3 + 2 * b2;
-  if (N == 8) return b3 + 2 * b2 + 4 * b1;
-  return b3 + 2 * b2 + 4 * b1 + 8 * b0;
-}
-
-template <int N>
-__device__ __forceinline__ bool ms_writer(int lane) {
-  if (lane >= 16) return false;
-  if (N == 1) return lane == 0;
-  if (N == 2) return (lane & 7) == 0;
-  if (N == 4) return (lane & 3) == 0;
-  if (N == 8) return (lane & 1) == 0;
-  return true;
-}
-
 // Where a unit lies: unit u covers rows [rloc_u, rloc_u + R*rpi) of the tile
 // (rows rloc_u + rg + rpi*i for the lane's row group rg) and column part
 // u % parts (chunks 64p .. 64p+63 of each row when a row has 128 chunks).

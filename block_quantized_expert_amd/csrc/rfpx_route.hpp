@@ -100,11 +100,14 @@ __device__ __forceinline__ void router_row(const float *wr, const void *x, int x
   }
   __shared__ float part[NT / 64][kQMax];
   const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int c = 0; c < kQMax; ++c) {
-    if (c >= q) break;
-    const float s = wave_sum_f32(acc[c]);
-    if (lane == 0) part[wave][c] = s;
+  // all columns' wave sums at once (DPP halving steps, multi_sum)
+  if (q == 1) {
+    const float v[1] = {acc[0]};
+    const float r = multi_sum<1>(v, lane);
+    if (lane == 0) part[wave][0] = r;
+  } else {
+    const float r = multi_sum<kQMax>(acc, lane);
+    if (ms_writer<kQMax>(lane)) part[wave][ms_index<kQMax>(lane)] = r;
   }
   __syncthreads();
   if (tid < q) {

@@ -45,18 +45,34 @@ __device__ void prep_item(const RouteArgs &a, int c, int b) {
   uint32_t *dst = a.xp + item * (size_t)a.vx * 16;
   uint32_t hi[32], lo[32], pw[16];
   float nc_hi, nc_lo = 0.f;
+  // the block's 32 activations in 16-byte loads (x is 16-byte aligned and
+  // d a multiple of 32, so every block starts on a 64-byte boundary)
   if (a.xtype == RFPX_X_BF16) {
-    const uint16_t *xs = static_cast<const uint16_t *>(a.x) + (size_t)c * a.d + 32 * b;
+    const uint4 *xs = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) +
+                                                      (size_t)c * a.d + 32 * b);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) hi[j] = xs[j];
+    for (int v = 0; v < 4; ++v) {
+      const uint4 w = xs[v];
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[8 * v + 2 * i] = wd[i] & 0xFFFFu;
+        hi[8 * v + 2 * i + 1] = wd[i] >> 16;
+      }
+    }
   } else {
     // fp32 activation = bf16 hi + bf16 lo (relative residual below 2^-16)
-    const float *xs = static_cast<const float *>(a.x) + (size_t)c * a.d + 32 * b;
+    const float4 *xs = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) +
+                                                        (size_t)c * a.d + 32 * b);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float v = xs[j];
-      hi[j] = float_to_bf16_rne(v);
-      lo[j] = float_to_bf16_rne(v - bf16_bits_to_float(hi[j]));
+    for (int v = 0; v < 8; ++v) {
+      const float4 w = xs[v];
+      const float wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[4 * v + i] = float_to_bf16_rne(wd[i]);
+        lo[4 * v + i] = float_to_bf16_rne(wd[i] - bf16_bits_to_float(hi[4 * v + i]));
+      }
     }
   }
   prep_pairs<FMT>(hi, pw, &nc_hi);
