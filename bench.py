@@ -334,17 +334,17 @@ def main() -> int:
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        n_cols = 0
+        n_steps = 0
         t = time.time()
         while True:
-            oracle.layer_forward_synth(lay0, x0_host[:1], "bf16")
-            n_cols += 1
+            oracle.layer_forward_synth(lay0, x0_host[:cfg.q], "bf16")
+            n_steps += 1
             if time.time() - t >= args.cpu_seconds:
                 break
         dt = time.time() - t
-        cpu = {"value": n_cols / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": (f"{n_cols} single-column decode steps of layer 0 (d={cfg.d}, "
-                          f"f={cfg.f}, E={cfg.E}, top-{cfg.k} + shared), plain C "
+        cpu = {"value": n_steps * cfg.q / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": (f"{n_steps} decode steps of {cfg.q} column(s) of layer 0 "
+                          f"(d={cfg.d}, f={cfg.f}, E={cfg.E}, top-{cfg.k} + shared), plain C "
                           f"oracle in double, single thread, {dt:.1f} s")}
 
     out = {
