@@ -623,53 +623,62 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
     const int jb0 = (c % CPS) * KC;
     // shift of this span's scales within their first piece
     const uint32_t sadd = (BS::SB * BS::SBY) % 16 ? (uint32_t)((c / CPS) * BS::SB * BS::SBY) % 16 : 0u;
-#pragma unroll 1
-    for (int j = 0; j < KC; ++j) {
-      if (c * KC + j < nblocks) {
-        const uint32_t *la = lds_a + (buf * KC + j) * ROWS * AWP;
-        const float *ln = lds_nc + (buf * KC + j) * ROWS;
-        const int jb = jb0 + j;
+    // one block: decode the B words of the wave's rows from LDS and run
+    // the products of every 16-row tile of A
+    auto block = [&](int j) __attribute__((always_inline)) {
+      const uint32_t *la = lds_a + (buf * KC + j) * ROWS * AWP;
+      const float *ln = lds_nc + (buf * KC + j) * ROWS;
+      const int jb = jb0 + j;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          bf16x8 bop[NM];
-          float bs[NM];
+      for (int nt = 0; nt < NT; ++nt) {
+        bf16x8 bop[NM];
+        float bs[NM];
 #pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            const uint8_t *cp = lds_b + lc[nt][m] + jb * BS::CB;
-            uint32_t q[3], pw[4];
-            q[0] = *reinterpret_cast<const uint32_t *>(cp);
-            if (FMT == RFPX_FP3) {
-              q[1] = *reinterpret_cast<const uint32_t *>(cp + 4);
-              q[2] = *reinterpret_cast<const uint32_t *>(cp + 8);
-            }
-            decode_quad<FMT>(qd, q, one, pw);
-            bop[m] = as_bf16x8(pw);
-            const uint32_t lsr = ls[nt][m] - (ls[nt][m] & 15u) + (((ls[nt][m] & 15u) + sadd) & 15u);
-            const uint8_t *sp = lds_b + lsr + jb * BS::SBY;
-            bs[m] = FMT == RFPX_FP4 ? block_scale<RFPX_FP4>(*sp)
-                                    : block_scale<FMT>(*reinterpret_cast<const uint16_t *>(sp));
+        for (int m = 0; m < NM; ++m) {
+          const uint8_t *cp = lds_b + lc[nt][m] + jb * BS::CB;
+          uint32_t q[3], pw[4];
+          q[0] = *reinterpret_cast<const uint32_t *>(cp);
+          if (FMT == RFPX_FP3) {
+            q[1] = *reinterpret_cast<const uint32_t *>(cp + 4);
+            q[2] = *reinterpret_cast<const uint32_t *>(cp + 8);
           }
+          decode_quad<FMT>(qd, q, one, pw);
+          bop[m] = as_bf16x8(pw);
+          const uint32_t lsr = ls[nt][m] - (ls[nt][m] & 15u) + (((ls[nt][m] & 15u) + sadd) & 15u);
+          const uint8_t *sp = lds_b + lsr + jb * BS::SBY;
+          bs[m] = FMT == RFPX_FP4 ? block_scale<RFPX_FP4>(*sp)
+                                  : block_scale<FMT>(*reinterpret_cast<const uint16_t *>(sp));
+        }
 #pragma unroll
-          for (int mt = 0; mt < NMT; ++mt) {
-            {
-              bf16x8 av[NA];
+        for (int mt = 0; mt < NMT; ++mt) {
+          {
+            bf16x8 av[NA];
 #pragma unroll
-              for (int v = 0; v < NA; ++v)
-                av[v] = __builtin_bit_cast(
-                    bf16x8, *reinterpret_cast<const u32x4 *>(la + (mt * 16 + col) * AWP + v * 16 + 4 * kq));
-              const floatx4 cin = *reinterpret_cast<const floatx4 *>(ln + mt * 16 + 4 * kq);
+            for (int v = 0; v < NA; ++v)
+              av[v] = __builtin_bit_cast(
+                  bf16x8, *reinterpret_cast<const u32x4 *>(la + (mt * 16 + col) * AWP + v * 16 + 4 * kq));
+            const floatx4 cin = *reinterpret_cast<const floatx4 *>(ln + mt * 16 + 4 * kq);
 #pragma unroll
-              for (int m = 0; m < NM; ++m) {
-                floatx4 pr = mfma(av[0], bop[m], cin);
+            for (int m = 0; m < NM; ++m) {
+              floatx4 pr = mfma(av[0], bop[m], cin);
 #pragma unroll
-                for (int v = 1; v < NA; ++v) pr = mfma(av[v], bop[m], pr);
+              for (int v = 1; v < NA; ++v) pr = mfma(av[v], bop[m], pr);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[mt][nt][m][i] = fmaf(bs[m], pr[i], acc[mt][nt][m][i]);
-              }
+              for (int i = 0; i < 4; ++i) acc[mt][nt][m][i] = fmaf(bs[m], pr[i], acc[mt][nt][m][i]);
             }
           }
         }
       }
+    };
+    if (c * KC + KC <= nblocks) {
+      // a full chunk: no per-block bounds branch (unrolling further raises
+      // the registers past two waves per SIMD and measures slower)
+#pragma unroll 1
+      for (int j = 0; j < KC; ++j) block(j);
+    } else {
+#pragma unroll 1
+      for (int j = 0; j < KC; ++j)
+        if (c * KC + j < nblocks) block(j);
     }
     if (c + 1 < nchunks) {
       store_a((c + 1) & 1);
