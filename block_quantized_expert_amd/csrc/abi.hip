@@ -155,6 +155,9 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   if (!pick_tile_down(p->geo_dn, p->down_fmts, p->g, L->d, dn_min < L->d ? dn_min : L->d,
                       &p->rw_dn))
     return fail(RFPX_E_SHAPE, "d=%d: no down tile for this format mix", L->d);
+  // per-wave accumulators of the down tile in LDS: fewer waves when a wide
+  // tile (short rows make long units) and many columns would not fit
+  while (p->wmax > 2 && (size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024) p->wmax /= 2;
   if ((size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024)
     return fail(RFPX_E_SHAPE, "f=%d, q=%d: down tile of %d rows needs too much LDS", L->f, q,
                 p->rw_dn);

@@ -136,6 +136,34 @@ def test_forward_rejects_arguments(lib):
     assert _fwd(lib, _layer(fmts=fm)) == -4
 
 
+def _pf(lib, L, x=0x10000, xtype=1, T=64, y=0x20000, ws=0x30000, nbytes=1 << 32):
+    return lib.moe_prefill_forward(L.ref, C.c_void_p(x), xtype, T, C.c_void_p(y),
+                                   C.c_void_p(ws), nbytes, None)
+
+
+def test_prefill_rejects_arguments(lib):
+    """Every check of moe_prefill_forward fails before any launch."""
+    L = _layer()
+    assert _pf(lib, L, T=0) == -2
+    assert _pf(lib, L, T=65537) == -2
+    assert _pf(lib, L, xtype=3) == -1
+    assert _pf(lib, L, x=0) == -1
+    assert _pf(lib, L, y=0) == -1
+    assert _pf(lib, L, ws=0) == -1
+    assert _pf(lib, L, ws=0x30010) == -3           # misaligned workspace
+    assert _pf(lib, L, x=0x10008) == -3            # misaligned x
+    assert _pf(lib, _layer(image=4096 + 64)) == -3
+    need = bqe.moe_workspace_bytes(L, 64, prefill=True)  # sized for fp32 x
+    assert need > 0
+    assert _pf(lib, L, xtype=0, nbytes=need - 1) == -5
+    assert b"workspace" in lib.rfpx_last_error()
+    fm = _fmts(8)
+    fm[3, 0] = 3  # gate FP3, up FP2
+    assert _pf(lib, _layer(fmts=fm)) == -4
+    # the prefill workspace grows with T, and fp32 x needs the most
+    assert bqe.moe_workspace_bytes(L, 128, prefill=True) > need
+
+
 def test_workspace_bytes_shapes(lib):
     L = _layer()
     n1 = bqe.moe_workspace_bytes(L, 1)

@@ -90,9 +90,12 @@ def test_tiny_bf16_activations(bqe, tiny):
 # ------------------------------------------------------- mixed small shapes
 
 @pytest.mark.parametrize("d,f,E,k,seed", [(512, 256, 16, 4, 1), (1024, 64, 32, 8, 2),
-                                           (256, 1024, 12, 3, 3), (4096, 128, 8, 2, 4)])
+                                           (256, 1024, 12, 3, 3), (4096, 128, 8, 2, 4),
+                                           (256, 4096, 8, 2, 5)])
 def test_mixed_formats_and_shapes(bqe, d, f, E, k, seed):
-    """Every format in every matrix position (gate/up FP3, down FP2, ...)."""
+    """Every format in every matrix position (gate/up FP3, down FP2, ...), one
+    to eight columns: q = 8 puts more columns in a slot than one pass covers,
+    and f = 4096 gives FP3/FP4 down rows two column parts."""
     cfg = synth.Config(0, "t", d, f, E, k, 1, "f32", "natural", scale_floor=1e-3,
                        master=100 + seed)
     lay = synth.gen_layer(cfg, 0, threads=4)
@@ -114,7 +117,7 @@ def test_mixed_formats_and_shapes(bqe, d, f, E, k, seed):
     lay.blob = np.concatenate(mats)
     L = bqe.upload_layer(lay)
     for xt in ("f32", "bf16"):
-        for q in (1, 3):
+        for q in (1, 3, 8):
             c2 = synth.Config(**{**cfg.__dict__, "xtype": xt})
             cols = synth.gen_columns(c2, lay, q, variant=q)
             y_ref, _, _ = _oracle(lay, cols.x, xt)
