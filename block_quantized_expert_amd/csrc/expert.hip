@@ -543,9 +543,15 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     sc.cols = rs.cols[slot];
     sc.w = rs.w[slot];
   } else {
-    route_wg(a.rp, &rs);
+    // routing in the workgroup; with one column slot s is rank s - 1
+    if (a.q == 1) route_q1(a.rp, &rs, slot);
+    else route_wg(a.rp, &rs);
     if (slot >= uniform(rs.nslots)) return;
-    if (blockIdx.x == 0) publish_route(rs, a.q, slot, slot == 1, a.rt);
+    if (blockIdx.x == 0) {
+      publish_route(rs, a.q, slot, slot == 1, a.rt);
+      if (threadIdx.x == 0) publish_down_desc(a.image, rs.expert[slot], slot, a.rt);
+      if (slot == 1 && threadIdx.x == 64) publish_down_desc(a.image, a.rp.E, 0, a.rt);
+    }
     sc.expert = uniform(rs.expert[slot]);
     sc.ncols = uniform(rs.ncols[slot]);
     sc.cols = rs.cols[slot];
@@ -788,12 +794,10 @@ __global__ __launch_bounds__(512) void k_down(ExpArgs a) {
   for (int i = threadIdx.x; i < nslots * (kQMax + 1); i += blockDim.x) {
     const int s = i / (kQMax + 1), j = i % (kQMax + 1);
     if (j == kQMax) {
-      const ExpertDesc *t =
-          reinterpret_cast<const ExpertDesc *>(a.image + kImgTable) + a.rt->expert[s];
       t_ncols[s] = a.rt->ncols[s];
-      t_codes[s] = t->codes[2];
-      t_scales[s] = t->scales[2];
-      t_fmt[s] = t->fmt[2];
+      t_codes[s] = a.rt->dn_codes[s];
+      t_scales[s] = a.rt->dn_scales[s];
+      t_fmt[s] = a.rt->dn_fmt[s];
     } else {
       t_cols[s][j] = a.rt->cols[s][j];
       t_w[s][j] = a.rt->w[s][j];

@@ -130,6 +130,11 @@ struct RouteTable {
   float w[kMaxSlots][kQMax];      // gating weight of cols[s][i]
   int32_t ids[kQMax][kKMax];      // top-k per column
   float gw[kQMax][kKMax];         // gating weight per column and rank
+  // each slot's down matrix in the image (from the expert table), so that
+  // the down kernel needs one dependent read instead of two
+  uint64_t dn_codes[kMaxSlots];
+  uint64_t dn_scales[kMaxSlots];
+  int32_t dn_fmt[kMaxSlots];
 };
 
 struct WsLayout {

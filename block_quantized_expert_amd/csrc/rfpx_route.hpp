@@ -229,18 +229,49 @@ __device__ __forceinline__ void topk_wave(const RouteParams &rp, int c, int lane
   }
 }
 
+// Sorted top-k and gating of column c by one wave (dispatch on E).
+__device__ __forceinline__ void topk_column(const RouteParams &rp, int c, int lane,
+                                            int32_t *s_ids, float *s_w) {
+  const int E = rp.E;
+  if (E <= 64) topk_wave<1>(rp, c, lane, s_ids, s_w);
+  else if (E <= 128) topk_wave<2>(rp, c, lane, s_ids, s_w);
+  else if (E <= 256) topk_wave<4>(rp, c, lane, s_ids, s_w);
+  else if (E <= 512) topk_wave<8>(rp, c, lane, s_ids, s_w);
+  else topk_wave<16>(rp, c, lane, s_ids, s_w);
+}
+
+// The routing step of a one-column step, for the workgroup of slot `slot`:
+// the k chosen experts are distinct, so slot s (1..k) is rank s - 1 and
+// there is nothing to deduplicate.  Fills the header fields, slot 0 and
+// the workgroup's own slot of the LDS table, exactly as route_wg would.
+// Ends with a barrier.
+__device__ __forceinline__ void route_q1(const RouteParams &rp, RouteLds *s, int slot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) topk_column(rp, 0, lane, s->ids[0], s->gw[0]);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    s->nslots = rp.k + 1;
+    s->expert[0] = rp.E;
+    s->ncols[0] = 1;
+    s->mask[0] = 1u;
+    s->cols[0][0] = 0;
+    s->w[0][0] = 1.0f;
+    if (slot >= 1 && slot <= rp.k) {
+      s->expert[slot] = s->ids[0][slot - 1];
+      s->ncols[slot] = 1;
+      s->mask[slot] = 1u;
+      s->cols[slot][0] = 0;
+      s->w[slot][0] = s->gw[0][slot - 1];
+    }
+  }
+  __syncthreads();
+}
+
 // Whole-workgroup routing into LDS; needs blockDim.x >= 64 * q.  Ends with a
 // barrier, so every thread may read the table afterwards.
 __device__ __forceinline__ void route_wg(const RouteParams &rp, RouteLds *s) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave < rp.q) {
-    const int E = rp.E;
-    if (E <= 64) topk_wave<1>(rp, wave, lane, s->ids[wave], s->gw[wave]);
-    else if (E <= 128) topk_wave<2>(rp, wave, lane, s->ids[wave], s->gw[wave]);
-    else if (E <= 256) topk_wave<4>(rp, wave, lane, s->ids[wave], s->gw[wave]);
-    else if (E <= 512) topk_wave<8>(rp, wave, lane, s->ids[wave], s->gw[wave]);
-    else topk_wave<16>(rp, wave, lane, s->ids[wave], s->gw[wave]);
-  }
+  if (wave < rp.q) topk_column(rp, wave, lane, s->ids[wave], s->gw[wave]);
   __syncthreads();
   if (wave == 0) {
     // lane i < n holds entry (column i / k, rank i % k); a slot per distinct
@@ -293,6 +324,16 @@ __device__ __forceinline__ void route_wg(const RouteParams &rp, RouteLds *s) {
     }
   }
   __syncthreads();
+}
+
+// The down-matrix entry of expert e's table row into slot `slot` of the
+// workspace table.
+__device__ __forceinline__ void publish_down_desc(const uint8_t *image, int e, int slot,
+                                                  RouteTable *rt) {
+  const ExpertDesc *t = reinterpret_cast<const ExpertDesc *>(image + kImgTable) + e;
+  rt->dn_codes[slot] = t->codes[2];
+  rt->dn_scales[slot] = t->scales[2];
+  rt->dn_fmt[slot] = t->fmt[2];
 }
 
 // Copy slot `slot` of the LDS table to the workspace table (slot < 0: all

@@ -112,6 +112,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a) {
 
 struct TopkArgs {
   RouteParams rp;
+  const uint8_t *image;
   RouteTable *rt;
   int32_t *ids_out;
   float *w_out;
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
       a.w_out[i] = s.gw[c][j];
     }
   publish_route(s, q, -1, true, a.rt);  // the whole table
+  if (a.image && tid < s.nslots) publish_down_desc(a.image, s.expert[tid], tid, a.rt);
 }
 
 }  // namespace
@@ -157,6 +159,7 @@ hipError_t launch_route(const ForwardPlan &p) {
   if (e != hipSuccess || !(p.route_only || p.pre_route)) return e;
   TopkArgs t{};
   t.rp = route_params(p);
+  t.image = p.image;
   t.rt = reinterpret_cast<RouteTable *>(p.ws + p.wl.route);
   t.ids_out = p.ids_out;
   t.w_out = p.w_out;
