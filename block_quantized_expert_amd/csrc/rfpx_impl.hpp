@@ -185,11 +185,13 @@ constexpr int kGuWavesQn = RFPX_GU_WAVES_QN, kGuRowsQn = RFPX_GU_ROWS_QN;
 constexpr int kDnWavesQn = RFPX_DN_WAVES_QN, kDnRowsQn = RFPX_DN_ROWS_QN;
 constexpr int kDnWavesQ1 = RFPX_DN_WAVES_Q1, kDnRowsQ1 = RFPX_DN_ROWS_Q1;
 
-// Gate/up units of steps of several columns are 4 rows: a wave keeps the
-// next unit's loads in flight while it decodes one (two register sets);
-// one-column steps keep single sets of unit_rows_for rows.
+// Gate/up units of steps of several columns are 2 rows: a wave keeps the
+// next unit's loads in flight while it decodes one (two register sets), and
+// 2-row sets keep the kernel at three waves per SIMD (4-row sets measured
+// 4% slower at two); one-column steps keep single sets of unit_rows_for
+// rows.
 __host__ __device__ constexpr int unit_rows_gu(int fmt, int g) {
-  return g == 1 ? unit_rows_for(fmt, 1) : 4;
+  return g == 1 ? unit_rows_for(fmt, 1) : 2;
 }
 
 // ------------------------------------------------------------ device side
