@@ -543,9 +543,9 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     sc.cols = rs.cols[slot];
     sc.w = rs.w[slot];
   } else {
-    // routing in the workgroup; with one column slot s is rank s - 1
-    if (a.q == 1) route_q1(a.rp, &rs, slot);
-    else route_wg(a.rp, &rs);
+    // one-column step: routing in the workgroup, slot s is rank s - 1
+    // (steps of several columns are always routed before the launch)
+    route_q1(a.rp, &rs, slot);
     if (slot >= uniform(rs.nslots)) return;
     if (blockIdx.x == 0) {
       publish_route(rs, a.q, slot, slot == 1, a.rt);

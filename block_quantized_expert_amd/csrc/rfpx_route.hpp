@@ -51,69 +51,94 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
-// Router scores s[c][e] = sum_i Wr[e][i] x[c][i] of one expert e for the q
+// Router scores s[c][e] = sum_i Wr[e][i] x[c][i] of one expert e for the Q
 // columns, by one workgroup of NT threads: thread t takes float4 groups t,
-// t + NT, ... of the row (d <= 4096), all loads issued before the
-// arithmetic (clamped indices, zeroed after, so no load waits on a branch);
-// the wave sums meet in LDS.
-template <int NT>
-__device__ __forceinline__ void router_row(const float *wr, const void *x, int xtype, int d,
-                                           int E, int q, float *scores, int e) {
+// t + NT, ... of the row (d <= 4096), counted from a start that rotates
+// with e (every workgroup reads the same x: with one start, all compute
+// units of an L2 would ask for the same lines, channel by channel, at the
+// same time).  Every load (the row and all Q columns of x) is issued before
+// the arithmetic, with clamped indices and zeroed after, so no load waits
+// on a branch or on another column's sums; the wave sums meet in LDS.
+template <int NT, int Q>
+__device__ __forceinline__ void router_row_q(const float *wr, const void *x, int xtype, int d,
+                                             int E, float *scores, int e) {
   constexpr int NPT = 4096 / 4 / NT;
   const int tid = threadIdx.x;
   const int n4 = d / 4;
+  // workgroups e, e + 8, ... share an L2 (the XCDs take workgroups in turn)
+  const int rot = (64 * (e >> 3)) % n4;
+  int idx[NPT];
+#pragma unroll
+  for (int j = 0; j < NPT; ++j) {
+    const int i4 = min(tid + NT * j, n4 - 1);  // w is zeroed past n4
+    idx[j] = i4 + rot < n4 ? i4 + rot : i4 + rot - n4;
+  }
   const float4 *wrow = reinterpret_cast<const float4 *>(wr + (size_t)e * d);
   float4 w[NPT];
 #pragma unroll
-  for (int j = 0; j < NPT; ++j) {
-    const int i4 = tid + NT * j;
-    w[j] = wrow[i4 < n4 ? i4 : n4 - 1];
-  }
+  for (int j = 0; j < NPT; ++j) w[j] = wrow[idx[j]];
+  float4 xv[Q][NPT];
 #pragma unroll
-  for (int j = 0; j < NPT; ++j)
-    if (tid + NT * j >= n4) w[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  float acc[kQMax];
-#pragma unroll
-  for (int c = 0; c < kQMax; ++c) {
-    acc[c] = 0.f;
-    if (c >= q) continue;
-    float4 xv[NPT];
+  for (int c = 0; c < Q; ++c)
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      const int i4 = min(tid + NT * j, n4 - 1);  // w is zero past n4
+      const int i4 = idx[j];
       if (xtype == RFPX_X_BF16) {
         const uint2 b = reinterpret_cast<const uint2 *>(
             static_cast<const uint16_t *>(x) + (size_t)c * d)[i4];
-        xv[j] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                            __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
+        xv[c][j] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
+                               __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u));
       } else {
-        xv[j] = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (size_t)c * d)[i4];
+        xv[c][j] = reinterpret_cast<const float4 *>(static_cast<const float *>(x) + (size_t)c * d)[i4];
       }
     }
 #pragma unroll
+  for (int j = 0; j < NPT; ++j)
+    if (tid + NT * j >= n4) w[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[Q];
+#pragma unroll
+  for (int c = 0; c < Q; ++c) {
+    acc[c] = 0.f;
+#pragma unroll
     for (int j = 0; j < NPT; ++j) {
-      acc[c] = fmaf(w[j].x, xv[j].x, acc[c]);
-      acc[c] = fmaf(w[j].y, xv[j].y, acc[c]);
-      acc[c] = fmaf(w[j].z, xv[j].z, acc[c]);
-      acc[c] = fmaf(w[j].w, xv[j].w, acc[c]);
+      acc[c] = fmaf(w[j].x, xv[c][j].x, acc[c]);
+      acc[c] = fmaf(w[j].y, xv[c][j].y, acc[c]);
+      acc[c] = fmaf(w[j].z, xv[c][j].z, acc[c]);
+      acc[c] = fmaf(w[j].w, xv[c][j].w, acc[c]);
     }
   }
-  __shared__ float part[NT / 64][kQMax];
+  __shared__ float part[NT / 64][Q];
   const int lane = tid & 63, wave = tid >> 6;
-  // all columns' wave sums at once (DPP halving steps, multi_sum)
-  if (q == 1) {
-    const float v[1] = {acc[0]};
-    const float r = multi_sum<1>(v, lane);
-    if (lane == 0) part[wave][0] = r;
-  } else {
-    const float r = multi_sum<kQMax>(acc, lane);
-    if (ms_writer<kQMax>(lane)) part[wave][ms_index<kQMax>(lane)] = r;
-  }
+  // all columns' wave sums at once (DPP halving steps, multi_sum, over a
+  // power-of-two count of values: zeros pad the columns past Q)
+  constexpr int QP = Q == 1 ? 1 : Q == 2 ? 2 : Q <= 4 ? 4 : 8;
+  float accp[QP];
+#pragma unroll
+  for (int c = 0; c < QP; ++c) accp[c] = c < Q ? acc[c] : 0.f;
+  const float r = multi_sum<QP>(accp, lane);
+  if (ms_writer<QP>(lane) && ms_index<QP>(lane) < Q) part[wave][ms_index<QP>(lane)] = r;
   __syncthreads();
-  if (tid < q) {
+  if (tid < Q) {
     float s = 0.f;
     for (int wv = 0; wv < NT / 64; ++wv) s += part[wv][tid];
     scores[(size_t)tid * E + e] = s;
+  }
+}
+
+// router_row_q for a run-time column count q = 1..kQMax.
+template <int NT>
+__device__ __forceinline__ void router_row(const float *wr, const void *x, int xtype, int d,
+                                           int E, int q, float *scores, int e) {
+  static_assert(kQMax == 8, "one case per column count");
+  switch (q) {
+    case 1: router_row_q<NT, 1>(wr, x, xtype, d, E, scores, e); break;
+    case 2: router_row_q<NT, 2>(wr, x, xtype, d, E, scores, e); break;
+    case 3: router_row_q<NT, 3>(wr, x, xtype, d, E, scores, e); break;
+    case 4: router_row_q<NT, 4>(wr, x, xtype, d, E, scores, e); break;
+    case 5: router_row_q<NT, 5>(wr, x, xtype, d, E, scores, e); break;
+    case 6: router_row_q<NT, 6>(wr, x, xtype, d, E, scores, e); break;
+    case 7: router_row_q<NT, 7>(wr, x, xtype, d, E, scores, e); break;
+    default: router_row_q<NT, 8>(wr, x, xtype, d, E, scores, e); break;
   }
 }
 
@@ -267,49 +292,60 @@ __device__ __forceinline__ void route_q1(const RouteParams &rp, RouteLds *s, int
   __syncthreads();
 }
 
-// Whole-workgroup routing into LDS; needs blockDim.x >= 64 * q.  Ends with a
-// barrier, so every thread may read the table afterwards.
-__device__ __forceinline__ void route_wg(const RouteParams &rp, RouteLds *s) {
+// Whole-workgroup routing into LDS; needs blockDim.x >= 64 * q and LDS
+// scratch of 2 E words.  Ends with a barrier, so every thread may read the
+// table afterwards.
+//
+// The q k entries (lane i of wave 0: column i / k, rank i % k) become one
+// slot per distinct expert, in order of first appearance, all lanes at
+// once: per expert, the lowest lane holding it (LDS atomic minimum) and the
+// set of columns that chose it (LDS atomic or).  A lane that is its
+// expert's first takes slot 1 + (number of first lanes below it); the
+// others read their first lane's slot.  A column picks an expert at most
+// once, so an entry's position in its slot is the number of the expert's
+// columns below its own, and the slot's columns ascend.
+__device__ __forceinline__ void route_wg(const RouteParams &rp, RouteLds *s, uint32_t *scr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave < rp.q) topk_column(rp, wave, lane, s->ids[wave], s->gw[wave]);
   __syncthreads();
   if (wave == 0) {
-    // lane i < n holds entry (column i / k, rank i % k); a slot per distinct
-    // expert, in order of first appearance
+    uint32_t *first = scr, *cmask = scr + rp.E;
     const int n = rp.q * rp.k;
-    int e = -1, c = 0;
+    const bool act = lane < n;
+    int e = 0, c = 0;
     float w = 0.f;
-    if (lane < n) {
+    if (act) {
       c = lane / rp.k;
       e = s->ids[c][lane % rp.k];
       w = s->gw[c][lane % rp.k];
+      first[e] = 64u;
+      cmask[e] = 0u;
     }
-    int first = lane;
-    for (int j = 0; j < n; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      if (lane < n && ej == e && j < first) first = j;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    if (act) {
+      atomicMin(&first[e], (uint32_t)lane);
+      atomicOr(&cmask[e], 1u << c);
     }
-    const bool is_first = lane < n && first == lane;
-    const uint64_t firsts = __ballot(is_first);
-    int slot = 1 + __popcll(firsts & ((1ull << lane) - 1ull));
-    slot = __shfl(slot, first, 64);
-    int pos = 0, cnt = 0;
-    uint32_t mask = 0;
-    for (int j = 0; j < n; ++j) {
-      const int sj = __builtin_amdgcn_readlane(slot, j), cj = __builtin_amdgcn_readlane(c, j);
-      if (sj == slot) {
-        ++cnt;
-        if (j < lane) ++pos;
-        mask |= 1u << cj;
-      }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    int f = lane;
+    uint32_t cm = 0;
+    if (act) {
+      f = (int)first[e];
+      cm = cmask[e];
     }
-    if (lane < n) {
+    const uint64_t firsts = __ballot(act && f == lane);
+    const int own = 1 + __popcll(firsts & ((1ull << lane) - 1ull));
+    const int slot = __shfl(own, f, 64);
+    if (act) {
+      const int pos = __popc(cm & ((1u << c) - 1u));
       s->cols[slot][pos] = c;
       s->w[slot][pos] = w;
-      if (is_first) {
+      if (f == lane) {
         s->expert[slot] = e;
-        s->ncols[slot] = cnt;
-        s->mask[slot] = mask;
+        s->ncols[slot] = __popc(cm);
+        s->mask[slot] = cm;
       }
     }
     if (lane == 0) {

@@ -118,11 +118,40 @@ struct TopkArgs {
   float *w_out;
 };
 
-__global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
+constexpr int kTopkThreads = 512;
+constexpr int kTopkDescPerThread = (kEMax + 1 + kTopkThreads - 1) / kTopkThreads;
+
+__global__ __launch_bounds__(kTopkThreads) void k_topk(TopkArgs a) {
   __shared__ RouteLds s;
-  route_wg(a.rp, &s);
+  __shared__ uint64_t dn_codes[kEMax + 1], dn_scales[kEMax + 1];
+  __shared__ int32_t dn_fmt[kEMax + 1];
+  __shared__ uint32_t scr[2 * kEMax];
   const int tid = threadIdx.x;
-  const int q = a.rp.q, k = a.rp.k;
+  const int q = a.rp.q, k = a.rp.k, E = a.rp.E;
+  // the down-matrix entries of the image table (shared expert included),
+  // loaded before the routing step so they arrive with the scores
+  const ExpertDesc *tab = a.image ? reinterpret_cast<const ExpertDesc *>(a.image + kImgTable) : nullptr;
+  uint64_t pc[kTopkDescPerThread], ps[kTopkDescPerThread];
+  int32_t pf[kTopkDescPerThread];
+#pragma unroll
+  for (int i = 0; i < kTopkDescPerThread; ++i) {
+    const int e = tid + kTopkThreads * i;
+    if (tab && e <= E) {
+      pc[i] = tab[e].codes[2];
+      ps[i] = tab[e].scales[2];
+      pf[i] = tab[e].fmt[2];
+    }
+  }
+  route_wg(a.rp, &s, scr);
+#pragma unroll
+  for (int i = 0; i < kTopkDescPerThread; ++i) {
+    const int e = tid + kTopkThreads * i;
+    if (tab && e <= E) {
+      dn_codes[e] = pc[i];
+      dn_scales[e] = ps[i];
+      dn_fmt[e] = pf[i];
+    }
+  }
   if (a.ids_out)
     for (int i = tid; i < q * k; i += blockDim.x) {
       const int c = i / k, j = i % k;
@@ -130,7 +159,13 @@ __global__ __launch_bounds__(512) void k_topk(TopkArgs a) {
       a.w_out[i] = s.gw[c][j];
     }
   publish_route(s, q, -1, true, a.rt);  // the whole table
-  if (a.image && tid < s.nslots) publish_down_desc(a.image, s.expert[tid], tid, a.rt);
+  __syncthreads();
+  if (tab && tid < s.nslots) {
+    const int e = s.expert[tid];
+    a.rt->dn_codes[tid] = dn_codes[e];
+    a.rt->dn_scales[tid] = dn_scales[e];
+    a.rt->dn_fmt[tid] = dn_fmt[e];
+  }
 }
 
 }  // namespace
@@ -163,7 +198,7 @@ hipError_t launch_route(const ForwardPlan &p) {
   t.rt = reinterpret_cast<RouteTable *>(p.ws + p.wl.route);
   t.ids_out = p.ids_out;
   t.w_out = p.w_out;
-  k_topk<<<1, 512, 0, p.stream>>>(t);
+  k_topk<<<1, kTopkThreads, 0, p.stream>>>(t);
   return hipGetLastError();
 }
 
