@@ -562,6 +562,13 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
 
 // ----------------------------------------------------------------- down
 
+// *p += v in LDS without waiting for the old value (ds_add_f32): the adds
+// of one wave to its own accumulator rows take effect in program order, so
+// the sums are the same from run to run.
+__device__ __forceinline__ void lds_add(float *p, float v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // One unit of one slot's down matrix for GP compact columns c0..: the
 // weighted row results are added into the wave's own accumulator rows
 // accw[column][row] (LDS, one writer lane per entry).
@@ -606,7 +613,7 @@ __device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, 
       const int i = n / GP, g = n % GP;
       const int cg = (GP == 2 && g) ? col[GP - 1] : col[0];
       const float wg = (GP == 2 && g) ? wgt[GP - 1] : wgt[0];
-      accw[cg * rw + up.rloc_u + i] += wg * v;
+      lds_add(&accw[cg * rw + up.rloc_u + i], wg * v);
     }
   } else {
 #pragma unroll
@@ -614,7 +621,7 @@ __device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, 
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const float v = group_sum(to[i][0][g], geo.lpr);
-        if (li == 0) accw[col[g] * rw + up.rloc_u + rg + geo.rpi * i] += wgt[g] * v;
+        if (li == 0) lds_add(&accw[col[g] * rw + up.rloc_u + rg + geo.rpi * i], wgt[g] * v);
       }
   }
 }
@@ -642,7 +649,7 @@ __device__ __forceinline__ void down_reduce(const float (&to)[R][1][GP], const G
       const int i = n / GP, g = n % GP;
       const int cg = (GP == 2 && g) ? col1 : col0;
       const float wg = (GP == 2 && g) ? wgt1 : wgt0;
-      accw[cg * rw + up.rloc_u + i] += wg * v;
+      lds_add(&accw[cg * rw + up.rloc_u + i], wg * v);
     }
   } else {
 #pragma unroll
@@ -650,7 +657,7 @@ __device__ __forceinline__ void down_reduce(const float (&to)[R][1][GP], const G
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const float v = group_sum(to[i][0][g], geo.lpr);
-        if (li == 0) accw[(g ? col1 : col0) * rw + up.rloc_u + rg + geo.rpi * i] += (g ? wgt1 : wgt0) * v;
+        if (li == 0) lds_add(&accw[(g ? col1 : col0) * rw + up.rloc_u + rg + geo.rpi * i], (g ? wgt1 : wgt0) * v);
       }
   }
 }

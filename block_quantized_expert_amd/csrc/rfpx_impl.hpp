@@ -218,11 +218,24 @@ __device__ __forceinline__ void ms_step(const float (&v)[N], float (&w)[N / 2], 
   }
 }
 
+// v[l] + v[l ^ 16] + v[l ^ 32] + v[l ^ 48] in every lane l, without LDS:
+// v_permlane16_swap / v_permlane32_swap with both operands v give the two
+// halves of each exchange, so one add completes it (fp32 addition is
+// commutative, so every lane of a pair gets the same bits).
+__device__ __forceinline__ float cross_row_sum(float r) {
+  const uint32_t u = __float_as_uint(r);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  r = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const uint32_t w = __float_as_uint(r);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
 // Sums of N values (N = 2, 4, 8, 16) over the 64 lanes of a wave, all at
 // once: log2(N) halving steps over lane bits 3, 2, 1, 0 (row_mirror,
 // row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2], in that order,
 // so that each step's partner agrees on every bit used before), plain DPP
-// sums over the remaining bits of a 16-lane row, and lane shuffles across
+// sums over the remaining bits of a 16-lane row, and cross_row_sum across
 // the four rows.  Lane l then holds the total of value ms_index<N>(l); the
 // lanes ms_writer<N>(l) hold each value once.  About 3N + 8 VALU ops
 // instead of 14 per value.
@@ -264,9 +277,7 @@ __device__ __forceinline__ float multi_sum(const float (&v)[N], int lane) {
       }
     }
   }
-  r += __shfl_xor(r, 16, 64);
-  r += __shfl_xor(r, 32, 64);
-  return r;
+  return cross_row_sum(r);
 }
 
 template <int N>
