@@ -124,6 +124,20 @@ def test_mixed_formats_and_shapes(bqe, d, f, E, k, seed):
             assert_close(_run(bqe, L, cols.x), y_ref, what=f"{xt} q={q}")
 
 
+def test_wide_router_shared_experts(bqe):
+    """E = 1024 experts, k = 8 and q = 8 Zipf-steered columns: a slot table
+    over the widest router with all 64 entries in use and experts repeated
+    across columns (43 distinct), built by the multi-column routing step."""
+    cfg = synth.Config(0, "wide", 1024, 64, 1024, 8, 8, "bf16", "zipf", scale_floor=1e-3,
+                       master=321)
+    lay = synth.gen_layer(cfg, 0, threads=4)
+    L = bqe.upload_layer(lay)
+    cols = synth.gen_columns(cfg, lay, 8)
+    assert len(set(cols.drawn.reshape(-1).tolist())) < 64
+    y_ref, _, _ = _oracle(lay, cols.x, "bf16")
+    assert_close(_run(bqe, L, cols.x), y_ref, what="E=1024 k=8 q=8")
+
+
 # ------------------------------------------------------ decode size (2, 3)
 
 @pytest.fixture(scope="module")
