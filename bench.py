@@ -4,11 +4,15 @@
 Metric: MoE-layer decode tokens/s (verify columns per second through one
 layer) and the packed expert bytes streamed per step as HBM GB/s.
 
-Workloads (synthetic, seeded; shapes of DeepSeek-V4-Flash-class layers):
-  --config 2  (default) q=1 decode: d=4096, f=2048, 256 experts top-6 + 1
-              shared; gate/up FP2, down FP3, shared FP4; bf16 activations
-  --config 3  q=4 verify columns, Zipf(1.1) routing per column
-  --config 4  q=5 verify columns, Zipf(1.1), 32 hottest experts FP4, 43 layers
+Workloads (synthetic, seeded; shapes of DeepSeek-V4-Flash-class layers),
+chosen with --workload:
+  decode-q1-d4096-e256-top6 (default)  q=1 decode: d=4096, f=2048, 256
+      experts top-6 + 1 shared; gate/up FP2, down FP3, shared FP4; bf16
+      activations
+  verify-q4-zipf  q=4 verify columns, Zipf(1.1) routing per column
+  verify-q5-zipf-hot32fp4-43layers  q=5 verify columns, Zipf(1.1), the 32
+      hottest experts FP4, 43 layers
+  prefill-t2048-zipf  a 2048-token prefill chunk through one layer
 A step is one moe_layer_forward call (router, top-k, batching, gate/up,
 down, combine) on one batch of q columns.  Steps rotate over --layers layer
 instances, each with its own router, experts and activations, so that no
@@ -185,7 +189,7 @@ def bench_prefill(args, cfg) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "config_id": cfg.cid, "tokens": cfg.q, "d": cfg.d,
+        "config": {"workload": cfg.name, "tokens": cfg.q, "d": cfg.d,
                    "f": cfg.f, "experts": cfg.E, "top_k": cfg.k, "shared": 1,
                    "formats": "gate/up FP2, down FP3, shared FP4", "activations": "bf16",
                    "layers_rotated": n_layers, "seed_master": cfg.master},
@@ -207,9 +211,12 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
+    ap.add_argument("--workload", default="decode-q1-d4096-e256-top6",
+                    choices=("decode-q1-d4096-e256-top6", "verify-q4-zipf",
+                             "verify-q5-zipf-hot32fp4-43layers", "prefill-t2048-zipf"))
     ap.add_argument("--layers", type=int, default=0,
-                    help="layer instances to rotate over (default 8; 43 for --config 4)")
+                    help="layer instances to rotate over (default 8; the workload's "
+                         "layer count when it names one, 43 for the q=5 workload)")
     ap.add_argument("--variants", type=int, default=4,
                     help="activation batches per layer instance")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -229,10 +236,10 @@ def main() -> int:
     import block_quantized_expert_amd as bqe
     import synth
 
-    cfg = synth.CONFIGS[args.config]
+    cfg = synth.WORKLOADS[args.workload]
     if cfg.prefill:
         return bench_prefill(args, cfg)
-    n_layers = args.layers or (43 if args.config == 4 else 8)
+    n_layers = args.layers or (cfg.layers if cfg.layers > 1 else 8)
     q = cfg.q
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -361,7 +368,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": cfg.name, "config_id": cfg.cid, "q": q, "d": cfg.d,
+            "workload": cfg.name, "q": q, "d": cfg.d,
             "f": cfg.f, "experts": cfg.E, "top_k": cfg.k, "shared": 1,
             "formats": ("gate/up FP2, down FP3, shared FP4"
                         + (", 32 hottest experts FP4" if cfg.hot_fp4 else "")),

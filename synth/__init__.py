@@ -53,7 +53,6 @@ _S_ROUTER, _S_MATRIX, _S_PERM, _S_X, _S_ZIPF = 0, 1, 2, 3, 4
 
 @dataclasses.dataclass(frozen=True)
 class Config:
-    cid: int
     name: str
     d: int
     f: int
@@ -70,17 +69,20 @@ class Config:
     master: int = 0
 
 
-CONFIGS = {
-    1: Config(1, "tiny-d256-e8-top2", 256, 128, 8, 2, 1, "f32", "natural",
-              scale_floor=1e-3, master=1),
-    2: Config(2, "decode-q1-d4096-e256-top6", 4096, 2048, 256, 6, 1, "bf16",
-              "natural", master=2),
-    3: Config(3, "verify-q4-zipf", 4096, 2048, 256, 6, 4, "bf16", "zipf",
-              master=3),
-    4: Config(4, "verify-q5-zipf-hot32fp4-43layers", 4096, 2048, 256, 6, 5,
-              "bf16", "zipf", hot_fp4=32, layers=43, master=4),
-    5: Config(5, "prefill-t2048-zipf", 4096, 2048, 256, 6, 2048, "bf16", "zipf",
-              prefill=True, master=5),
+TINY = "tiny-d256-e8-top2"
+DECODE_Q1 = "decode-q1-d4096-e256-top6"
+VERIFY_Q4 = "verify-q4-zipf"
+VERIFY_Q5 = "verify-q5-zipf-hot32fp4-43layers"
+PREFILL = "prefill-t2048-zipf"
+
+WORKLOADS = {
+    TINY: Config(TINY, 256, 128, 8, 2, 1, "f32", "natural", scale_floor=1e-3, master=1),
+    DECODE_Q1: Config(DECODE_Q1, 4096, 2048, 256, 6, 1, "bf16", "natural", master=2),
+    VERIFY_Q4: Config(VERIFY_Q4, 4096, 2048, 256, 6, 4, "bf16", "zipf", master=3),
+    VERIFY_Q5: Config(VERIFY_Q5, 4096, 2048, 256, 6, 5, "bf16", "zipf", hot_fp4=32,
+                      layers=43, master=4),
+    PREFILL: Config(PREFILL, 4096, 2048, 256, 6, 2048, "bf16", "zipf", prefill=True,
+                    master=5),
 }
 
 

@@ -192,7 +192,7 @@ def test_status_strings(lib):
 
 
 def test_generator_layer_shapes_match_library(lib):
-    lay = synth.gen_layer(synth.CONFIGS[1], 0, threads=2)
+    lay = synth.gen_layer(synth.WORKLOADS[synth.TINY], 0, threads=2)
     for e in range(lay.E + 1):
         for m in range(3):
             rows, cols = lay.matrix_shape(m)

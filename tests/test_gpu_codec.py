@@ -79,7 +79,7 @@ def test_empty_matrix(bqe):
 
 @pytest.fixture(scope="module")
 def tiny(bqe):
-    lay = synth.gen_layer(synth.CONFIGS[1], 0, threads=4)
+    lay = synth.gen_layer(synth.WORKLOADS[synth.TINY], 0, threads=4)
     return lay, bqe.upload_layer(lay)
 
 
@@ -95,7 +95,7 @@ def test_image_roundtrip_tiny_every_matrix(bqe, tiny):
 
 def test_image_roundtrip_decode_size_sample(bqe):
     import torch
-    lay = synth.gen_layer(synth.CONFIGS[4], 3)  # mixed FP2/FP3/FP4 layer
+    lay = synth.gen_layer(synth.WORKLOADS[synth.VERIFY_Q5], 3)  # mixed FP2/FP3/FP4 layer
     L = bqe.upload_layer(lay)
     hot = int(lay.perm[0])
     for e in (0, hot, 131, lay.E - 1, lay.E):

@@ -31,11 +31,11 @@ def _oracle(lay, x_np, xtype):
     return oracle.layer_forward_synth(lay, x_np, xtype)
 
 
-# ------------------------------------------------------------- tiny (cfg 1)
+# ------------------------------------------------- tiny layer, d=256, E=8
 
 @pytest.fixture(scope="module")
 def tiny(bqe):
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[synth.TINY]
     lay = synth.gen_layer(cfg, 0, threads=4)
     return cfg, lay, bqe.upload_layer(lay)
 
@@ -96,7 +96,7 @@ def test_mixed_formats_and_shapes(bqe, d, f, E, k, seed):
     """Every format in every matrix position (gate/up FP3, down FP2, ...), one
     to eight columns: q = 8 puts more columns in a slot than one pass covers,
     and f = 4096 gives FP3/FP4 down rows two column parts."""
-    cfg = synth.Config(0, "t", d, f, E, k, 1, "f32", "natural", scale_floor=1e-3,
+    cfg = synth.Config("t", d, f, E, k, 1, "f32", "natural", scale_floor=1e-3,
                        master=100 + seed)
     lay = synth.gen_layer(cfg, 0, threads=4)
     # rewrite the format table: cycle formats, regenerate those matrices
@@ -128,7 +128,7 @@ def test_wide_router_shared_experts(bqe):
     """E = 1024 experts, k = 8 and q = 8 Zipf-steered columns: a slot table
     over the widest router with all 64 entries in use and experts repeated
     across columns (43 distinct), built by the multi-column routing step."""
-    cfg = synth.Config(0, "wide", 1024, 64, 1024, 8, 8, "bf16", "zipf", scale_floor=1e-3,
+    cfg = synth.Config("wide", 1024, 64, 1024, 8, 8, "bf16", "zipf", scale_floor=1e-3,
                        master=321)
     lay = synth.gen_layer(cfg, 0, threads=4)
     L = bqe.upload_layer(lay)
@@ -138,12 +138,12 @@ def test_wide_router_shared_experts(bqe):
     assert_close(_run(bqe, L, cols.x), y_ref, what="E=1024 k=8 q=8")
 
 
-# ------------------------------------------------------ decode size (2, 3)
+# ---------------------------------------- decode size, d=4096, f=2048, E=256
 
 @pytest.fixture(scope="module")
 def decode_layer(bqe):
     import torch
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS[synth.DECODE_Q1]
     lay = synth.gen_layer(cfg, 0)
     L = bqe.upload_layer(lay)
     yield cfg, lay, L
@@ -162,7 +162,7 @@ def test_decode_q1(bqe, decode_layer):
 
 def test_verify_q4_zipf(bqe, decode_layer):
     cfg2, lay, L = decode_layer
-    cfg = synth.CONFIGS[3]
+    cfg = synth.WORKLOADS[synth.VERIFY_Q4]
     cols = synth.gen_columns(cfg, lay, 4)
     with cf.ThreadPoolExecutor(4) as ex:
         refs = list(ex.map(lambda c: _oracle(lay, cols.x[c:c + 1], "bf16")[0], range(4)))
@@ -170,12 +170,12 @@ def test_verify_q4_zipf(bqe, decode_layer):
     assert_close(_run(bqe, L, cols.x), y_ref, what="q=4")
 
 
-# ------------------------------------------------------ q=5 mixed (cfg 4)
+# ------------------------------------- q=5 with the 32 hottest experts FP4
 
 @pytest.mark.parametrize("layer", [0, 21, 42])
 def test_verify_q5_hot_fp4(bqe, layer):
     import torch
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS[synth.VERIFY_Q5]
     lay = synth.gen_layer(cfg, layer)
     L = bqe.upload_layer(lay)
     cols = synth.gen_columns(cfg, lay, 5, layer=layer)

@@ -55,7 +55,7 @@ def _oracle_rows(lay, x, xtype, rows=None, threads=8):
 
 def _mixed_layer(d, f, E, k, seed):
     """A layer whose format table cycles every format through every matrix."""
-    cfg = synth.Config(0, "t", d, f, E, k, 1, "f32", "natural", scale_floor=1e-3,
+    cfg = synth.Config("t", d, f, E, k, 1, "f32", "natural", scale_floor=1e-3,
                        master=200 + seed)
     lay = synth.gen_layer(cfg, 0, threads=4)
     rng = np.random.default_rng(seed)
@@ -76,7 +76,7 @@ def _mixed_layer(d, f, E, k, seed):
 
 
 def test_prefill_tiny_every_token(bqe):
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[synth.TINY]
     lay = synth.gen_layer(cfg, 0, threads=4)
     L = bqe.upload_layer(lay)
     for xt, T in (("f32", 64), ("bf16", 37)):
@@ -100,7 +100,7 @@ def test_prefill_mixed_formats(bqe, d, f, E, k, T, seed):
 
 def test_prefill_single_token_and_one_expert(bqe):
     # T = 1; and E = k = 1 (every token picks the only routed expert)
-    cfg = synth.Config(0, "t", 256, 128, 1, 1, 1, "bf16", "natural", scale_floor=1e-3, master=300)
+    cfg = synth.Config("t", 256, 128, 1, 1, 1, "bf16", "natural", scale_floor=1e-3, master=300)
     lay = synth.gen_layer(cfg, 0, threads=4)
     L = bqe.upload_layer(lay)
     for T in (1, 5, 130):
@@ -121,7 +121,7 @@ def test_prefill_2048_tokens_zipf_sampled(bqe):
     every row checked against the decode path for 64 sampled tokens, and a
     sample of 12 tokens against the oracle."""
     import torch
-    cfg = synth.CONFIGS[5]
+    cfg = synth.WORKLOADS[synth.PREFILL]
     lay = synth.gen_layer(cfg, 0)
     L = bqe.upload_layer(lay)
     cols = synth.gen_columns(cfg, lay, cfg.q)

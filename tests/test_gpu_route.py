@@ -42,12 +42,12 @@ def _check(bqe, L, wr, k, x_np, xtype):
     return ids
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
-def test_route_configs(bqe, cid):
-    cfg = synth.CONFIGS[cid]
+@pytest.mark.parametrize("name", [synth.TINY, synth.DECODE_Q1, synth.VERIFY_Q4, synth.VERIFY_Q5])
+def test_route_workloads(bqe, name):
+    cfg = synth.WORKLOADS[name]
     wr, perm = synth.gen_router(cfg, 0)
     L = _router_layer(bqe, wr, cfg.k, f=cfg.f)
-    q = 4 if cid == 1 else cfg.q
+    q = 4 if name == synth.TINY else cfg.q
     for variant in range(3):
         cols = synth.gen_columns(cfg, (wr, perm, cfg.k), q, variant=variant)
         ids = _check(bqe, L, wr, cfg.k, cols.x, cfg.xtype)
@@ -56,7 +56,7 @@ def test_route_configs(bqe, cid):
 
 
 def test_route_prefill_tokens_in_chunks(bqe):
-    cfg = synth.CONFIGS[5]
+    cfg = synth.WORKLOADS[synth.PREFILL]
     wr, perm = synth.gen_router(cfg, 0)
     L = _router_layer(bqe, wr, cfg.k, f=cfg.f)
     cols = synth.gen_columns(cfg, (wr, perm, cfg.k), 256)
@@ -86,7 +86,7 @@ def test_route_ties_go_to_lower_index(bqe):
 def test_route_edge_sizes(bqe, E, k, q):
     rng = np.random.default_rng(E + k + q)
     wr = (rng.standard_normal((E, 512)) * 0.02).astype(np.float32)
-    cfg = synth.Config(0, "t", 512, 128, E, k, q, "f32", "natural", master=E)
+    cfg = synth.Config("t", 512, 128, E, k, q, "f32", "natural", master=E)
     cols = synth.gen_columns(cfg, (wr, np.arange(E), k), q)
     L = _router_layer(bqe, wr, k)
     _check(bqe, L, wr, k, cols.x, "f32")

@@ -342,7 +342,7 @@ def test_layer_closed_form():
 
 
 def _tiny_layer(seed=0, d=96, f=64, E=6, k=2, fp4_expert=None):
-    cfg = synth.Config(0, "t", d, f, E, k, 1, "f32", "natural",
+    cfg = synth.Config("t", d, f, E, k, 1, "f32", "natural",
                        scale_floor=1e-3, master=seed,
                        hot_fp4=0 if fp4_expert is None else 1)
     return synth.gen_layer(cfg, 0, threads=2), cfg

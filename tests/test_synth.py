@@ -17,7 +17,7 @@ def test_same_seed_same_bytes():
 
 
 def test_tiny_layer_sizes_and_formats():
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[synth.TINY]
     lay = synth.gen_layer(cfg, 0, threads=2)
     assert lay.fmts.shape == (9, 3)
     assert list(lay.fmts[0]) == [2, 2, 3] and list(lay.fmts[8]) == [4, 4, 4]
@@ -30,7 +30,7 @@ def test_tiny_layer_sizes_and_formats():
 
 
 def test_scale_distribution_tiny():
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[synth.TINY]
     lay = synth.gen_layer(cfg, 0, threads=2)
     g = lay.mat(0, 0).reshape(-1, 10)
     s = g[:, 8:].copy().view(np.float16).astype(np.float64).reshape(-1)
@@ -39,7 +39,7 @@ def test_scale_distribution_tiny():
 
 
 def test_hot_experts_fp4():
-    cfg = synth.CONFIGS[4]
+    cfg = synth.WORKLOADS[synth.VERIFY_Q5]
     wr, perm = synth.gen_router(cfg, 7)
     fm = synth.expert_formats(cfg.E, perm, cfg.hot_fp4)
     assert set(np.flatnonzero(fm[:256, 0] == 4)) == set(perm[:32].tolist())
@@ -58,7 +58,7 @@ def _check_columns(cfg, wr, perm, cols, k):
 
 
 def test_natural_routing_gap_guard_tiny():
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[synth.TINY]
     wr, perm = synth.gen_router(cfg, 0)
     cols = synth.gen_columns(cfg, (wr, perm, cfg.k), 16)
     assert cols.x.dtype == np.float32
@@ -66,16 +66,16 @@ def test_natural_routing_gap_guard_tiny():
 
 
 def test_natural_routing_gap_guard_decode():
-    cfg = synth.CONFIGS[2]
+    cfg = synth.WORKLOADS[synth.DECODE_Q1]
     wr, perm = synth.gen_router(cfg, 0)
     cols = synth.gen_columns(cfg, (wr, perm, cfg.k), 8)
     assert cols.x.dtype == np.uint16
     _check_columns(cfg, wr, perm, cols, cfg.k)
 
 
-@pytest.mark.parametrize("cid", [3, 4])
-def test_zipf_routing_is_realized_by_the_oracle(cid):
-    cfg = synth.CONFIGS[cid]
+@pytest.mark.parametrize("name", [synth.VERIFY_Q4, synth.VERIFY_Q5])
+def test_zipf_routing_is_realized_by_the_oracle(name):
+    cfg = synth.WORKLOADS[name]
     wr, perm = synth.gen_router(cfg, 1)
     cols = synth.gen_columns(cfg, (wr, perm, cfg.k), cfg.q, layer=1)
     _check_columns(cfg, wr, perm, cols, cfg.k)
