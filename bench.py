@@ -151,6 +151,7 @@ def bench_prefill(args, cfg) -> int:
     steps = min(args.steps, 40)
     warm = min(args.warmup, 4)
     layers = []
+    lay0 = x0_host = None
     for l in range(n_layers):
         lay = synth.gen_layer(cfg, l)
         L = bqe.upload_layer(lay)
@@ -158,6 +159,8 @@ def bench_prefill(args, cfg) -> int:
         x = torch.from_numpy(cols.x.view(np.int16)).view(torch.bfloat16).to(dev)
         layers.append((L, x, bqe.workspace(L, cfg.q, prefill=True)))
         weight_bytes = int(lay.blob.size)
+        if l == 0 and args.cpu_seconds > 0:
+            lay0, x0_host = lay, cols.x
         del lay
         print(f"# layer {l + 1}/{n_layers} ready", file=sys.stderr, flush=True)
     y = torch.empty((cfg.q, cfg.d), dtype=torch.float32, device=dev)
@@ -176,6 +179,25 @@ def bench_prefill(args, cfg) -> int:
     ms = t0.elapsed_time(t1) / steps
     rows = cfg.q * (cfg.k + 1)
     flops = 2.0 * rows * 3 * cfg.f * cfg.d  # gate, up and down of every (token, expert) row
+
+    # ---- CPU oracle on a bounded sample of the chunk: its first tokens, a
+    # few at a time (each token is routed and computed on its own)
+    cpu = None
+    if lay0 is not None:
+        import oracle
+        per, n_tok = 4, 0
+        t = time.time()
+        while n_tok + per <= cfg.q:
+            oracle.layer_forward_synth(lay0, x0_host[n_tok:n_tok + per], "bf16")
+            n_tok += per
+            if time.time() - t >= args.cpu_seconds:
+                break
+        dt = time.time() - t
+        cpu = {"value": n_tok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": (f"the first {n_tok} of the {cfg.q} tokens of layer 0 "
+                          f"(d={cfg.d}, f={cfg.f}, E={cfg.E}, top-{cfg.k} + shared), plain C "
+                          f"oracle in double, single thread, {dt:.1f} s")}
+        del lay0
     out = {
         "metric": "MoE-layer prefill tokens/s (2048-token chunk) and MFMA utilization",
         "value": cfg.q / (ms * 1e-3),
@@ -200,7 +222,7 @@ def bench_prefill(args, cfg) -> int:
                      "frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                      "traffic": None, "kernel": "whole prefill chunk (all launches)"},
         "weight_GB_per_s": weight_bytes / (ms * 1e-3) / 1e9,
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out))
     return 0
