@@ -127,10 +127,15 @@ __global__ __launch_bounds__(256) void k_pf_scores(PfArgs a) {
   const int t = min(t0 + col, a.T - 1);
   const int er[2] = {min(e0 + col, a.E - 1), min(e0 + 16 + col, a.E - 1)};
   floatx4 acc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-  float xn[8], wn[2][8];
-  auto load = [&](int k0) {
+  // a ring of NS steps of 32: the loads of step s + NS - 1 go out while step
+  // s is multiplied, so about NS - 1 steps of loads are in flight (one wave
+  // per SIMD: there is no other wave to cover the latency).  d is a multiple
+  // of 32 NS, and the ring index of every step is a compile-time constant.
+  constexpr int NS = 4;
+  float xn[NS][8], wn[NS][2][8];
+  auto load = [&](int k0, float (&xb)[8], float (&wb)[2][8]) __attribute__((always_inline)) {
     const int k = k0 + 8 * kq;
-    scores_load<XT>(a, t, k, xn);
+    scores_load<XT>(a, t, k, xb);
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const float *p = a.wr + (size_t)er[n] * a.d + k;
@@ -138,26 +143,24 @@ __global__ __launch_bounds__(256) void k_pf_scores(PfArgs a) {
       const floatx4 v1 = *reinterpret_cast<const floatx4 *>(p + 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        wn[n][i] = v0[i];
-        wn[n][4 + i] = v1[i];
+        wb[n][i] = v0[i];
+        wb[n][4 + i] = v1[i];
       }
     }
   };
-  load(0);
-  for (int k0 = 0; k0 < a.d; k0 += 32) {
-    float xc[8], wc[2][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xc[i] = xn[i];
-      wc[0][i] = wn[0][i];
-      wc[1][i] = wn[1][i];
+  for (int st = 0; st < NS - 1; ++st) load(32 * st, xn[st], wn[st]);
+  for (int k0 = 0; k0 < a.d; k0 += 32 * NS) {
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
+      const int kn = k0 + 32 * (st + NS - 1);
+      if (kn < a.d) load(kn, xn[(st + NS - 1) % NS], wn[(st + NS - 1) % NS]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(xn[st][s], wn[st][n][s], acc[n], 0, 0, 0);
     }
-    if (k0 + 32 < a.d) load(k0 + 32);
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(xc[s], wc[n][s], acc[n], 0, 0, 0);
   }
   // D[4 kq + i][col]: token t0 + 4 kq + i, expert e0 + 16 n + col
 #pragma unroll
