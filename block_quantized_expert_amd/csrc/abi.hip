@@ -289,8 +289,8 @@ rfpx_status moe_prefill_forward(const moe_layer *L, const void *x, int xtype, in
   if (!x || !y || !ws) return fail(RFPX_E_ARG, "x, y or workspace is null");
   if ((uintptr_t)ws % 256) return fail(RFPX_E_ALIGN, "workspace not 256-byte aligned");
   if ((uintptr_t)L->image % 256) return fail(RFPX_E_ALIGN, "image not 256-byte aligned");
-  if ((uintptr_t)L->router_w % 16 || (uintptr_t)x % 16)
-    return fail(RFPX_E_ALIGN, "router weights and x must be 16-byte aligned");
+  if ((uintptr_t)L->router_w % 16 || (uintptr_t)x % 16 || (uintptr_t)y % 16)
+    return fail(RFPX_E_ALIGN, "router weights, x and y must be 16-byte aligned");
   if (ws_bytes < need)
     return fail(RFPX_E_WORKSPACE, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
   const size_t image_bytes = image_layout(L->d, L->f, L->n_experts, L->fmts, nullptr);

@@ -883,13 +883,25 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(PfArgs a) {
 
 // ---------------------------------------------------------------- combine
 
+// Four outputs per thread (d is a multiple of 4): the loads of every rank
+// are issued before the sums, which run in rank order.
 __global__ __launch_bounds__(256) void k_pf_combine(PfArgs a) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (size_t)a.T * a.d) return;
-  const size_t t = i / a.d, n = i % a.d;
-  float v = 0.f;
-  for (int r = 0; r <= a.k; ++r) v += a.out[(t * (a.k + 1) + r) * a.d + n];
-  a.y[i] = v;
+  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i4 >= (size_t)a.T * a.d / 4) return;
+  const size_t t = i4 * 4 / a.d, n = i4 * 4 % a.d;
+  const floatx4 *src = reinterpret_cast<const floatx4 *>(a.out + t * (a.k + 1) * a.d + n);
+  const size_t rstride = (size_t)a.d / 4;
+  floatx4 o[kKMax + 1];
+#pragma unroll
+  for (int r = 0; r <= kKMax; ++r)
+    if (r <= a.k) o[r] = src[r * rstride];
+  floatx4 v = o[0];
+#pragma unroll
+  for (int r = 1; r <= kKMax; ++r)
+    if (r <= a.k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += o[r][j];
+  *reinterpret_cast<floatx4 *>(a.y + i4 * 4) = v;
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -1014,7 +1026,7 @@ hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, f
   if (a.vx == 1) k_pf_gateup<1><<<ggu, kPfThreads, 0, stream>>>(a);
   else k_pf_gateup<2><<<ggu, kPfThreads, 0, stream>>>(a);
   k_pf_down<<<gdn, kPfThreads, 0, stream>>>(a);
-  k_pf_combine<<<(unsigned)(((size_t)T * a.d + 255) / 256), 256, 0, stream>>>(a);
+  k_pf_combine<<<(unsigned)(((size_t)T * a.d / 4 + 255) / 256), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -195,8 +195,9 @@ rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x_dev,
  * grouped by expert and each expert runs as a dense grouped product on the
  * matrix cores.  y_dev[T][d] fp32.  ([P3] "稀疏预填充": prefill is batched per
  * layer.)  T in [1, 65536]; d a multiple of 128 and f of 64; the image at
- * most 4 GiB; ws_bytes at least moe_workspace_bytes(L, T, 1).  A violated
- * limit returns RFPX_E_SHAPE / RFPX_E_WORKSPACE before any launch. */
+ * most 4 GiB; x_dev and y_dev 16-byte aligned; ws_bytes at least
+ * moe_workspace_bytes(L, T, 1).  A violated limit returns RFPX_E_SHAPE /
+ * RFPX_E_ALIGN / RFPX_E_WORKSPACE before any launch. */
 rfpx_status moe_prefill_forward(const moe_layer *L, const void *x_dev,
                                 int xtype, int T, float *y_dev, void *ws_dev,
                                 size_t ws_bytes, void *stream);

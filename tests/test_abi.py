@@ -152,6 +152,7 @@ def test_prefill_rejects_arguments(lib):
     assert _pf(lib, L, ws=0) == -1
     assert _pf(lib, L, ws=0x30010) == -3           # misaligned workspace
     assert _pf(lib, L, x=0x10008) == -3            # misaligned x
+    assert _pf(lib, L, y=0x20004) == -3            # misaligned y
     assert _pf(lib, _layer(image=4096 + 64)) == -3
     need = bqe.moe_workspace_bytes(L, 64, prefill=True)  # sized for fp32 x
     assert need > 0
