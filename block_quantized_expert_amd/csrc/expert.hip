@@ -298,16 +298,21 @@ __device__ __forceinline__ void gateup_reduce(const float (&tot)[R][2][GP], cons
   const int rg = lane / geo.lpr, li = lane % geo.lpr;
   if (geo.lpr == 64) {  // one row per wave step: reduce all values at once
     constexpr int N = R * 2 * GP;
-    float flat[N];
+    // multi_sum takes a power-of-two count: zeros pad the values past N
+    constexpr int NP = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : 16;
+    static_assert(N <= 16, "at most 16 values per unit");
+    float flat[NP];
+#pragma unroll
+    for (int n = N; n < NP; ++n) flat[n] = 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int g = 0; g < GP; ++g) flat[(i * 2 + m) * GP + g] = tot[i][m][g];
-    const float v = multi_sum<N>(flat, lane);
-    if (ms_writer<N>(lane)) {
-      const int n = ms_index<N>(lane);
+    const float v = multi_sum<NP>(flat, lane);
+    const int n = ms_index<NP>(lane);
+    if (ms_writer<NP>(lane) && n < N) {
       const int i = n / (2 * GP), m = (n / GP) % 2, g = n % GP;
       gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + i] = v;
     }
@@ -442,14 +447,24 @@ __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc
   const int units = rw / (R * geo.rpi) * P;
   const int wave = uniform(threadIdx.x >> 6);
   const int waves = blockDim.x >> 6;
-  // FP2 chunks hold two blocks: with fp32 activations (hi + lo) two-column
-  // passes would need 128 registers of activations, so those take one
-  constexpr int GD = (FMT == RFPX_FP2 && VX == 2) ? 1 : G;
+  // columns per pass: 64 registers of prepared activations per lane, i.e.
+  // two columns of FP2 chunks (two blocks each) or four of FP3/FP4 chunks
+  // (one block), halved for fp32 activations (hi + lo)
+  constexpr int GD = G == 1 ? 1 : (FMT == RFPX_FP2 ? 2 : 4) / VX;
   for (int c0 = 0; c0 < sc.ncols; c0 += GD) {
-    const int gc = (GD == 2 && sc.ncols - c0 >= 2) ? 2 : 1;
+    const int gc = sc.ncols - c0 < GD ? sc.ncols - c0 : GD;
     if (wave < units) {
       if constexpr (G == 1) {
         gateup_pass1<FMT, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
+      } else if constexpr (GD == 4) {
+        if (gc == 4)
+          gateup_pass<FMT, 4, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
+        else if (gc == 3)
+          gateup_pass<FMT, 3, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
+        else if (gc == 2)
+          gateup_pass<FMT, 2, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
+        else
+          gateup_pass<FMT, 1, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
       } else if constexpr (GD == 2) {
         if (gc == 2)
           gateup_pass<FMT, 2, VX, R>(a, sc, c0, geo, units, wave, waves, tile, mats, cpitch, spitch, gup);
