@@ -174,31 +174,48 @@ __global__ __launch_bounds__(256) void k_pf_scores(PfArgs a) {
 
 // ------------------------------------------------- prepared activations
 
+// (x is 16-byte aligned and d a multiple of 128, so a block of x starts on
+// a 64-byte boundary and its prepared words on a 64-byte boundary too.)
 template <int FMT>
 __device__ void pf_prep_item(const PfArgs &a, int slot, int t, int b) {
   uint32_t hi[32], lo[32], pw[16];
   float nc_hi, nc_lo = 0.f;
   if (a.xtype == RFPX_X_BF16) {
-    const uint16_t *xs = static_cast<const uint16_t *>(a.x) + (size_t)t * a.d + 32 * b;
+    const uint4 *xs = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.x) +
+                                                      (size_t)t * a.d + 32 * b);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) hi[j] = xs[j];
+    for (int v = 0; v < 4; ++v) {
+      const uint4 w = xs[v];
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[8 * v + 2 * i] = wd[i] & 0xFFFFu;
+        hi[8 * v + 2 * i + 1] = wd[i] >> 16;
+      }
+    }
   } else {
-    const float *xs = static_cast<const float *>(a.x) + (size_t)t * a.d + 32 * b;
+    const float4 *xs = reinterpret_cast<const float4 *>(static_cast<const float *>(a.x) +
+                                                        (size_t)t * a.d + 32 * b);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float v = xs[j];
-      hi[j] = float_to_bf16_rne(v);
-      lo[j] = float_to_bf16_rne(v - bf16_bits_to_float(hi[j]));
+    for (int v = 0; v < 8; ++v) {
+      const float4 w = xs[v];
+      const float wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hi[4 * v + i] = float_to_bf16_rne(wd[i]);
+        lo[4 * v + i] = float_to_bf16_rne(wd[i] - bf16_bits_to_float(hi[4 * v + i]));
+      }
     }
   }
-  uint32_t *dst = a.xp + (((size_t)slot * a.T + t) * a.nb_d + b) * a.vx * 16;
+  uint4 *dst = reinterpret_cast<uint4 *>(a.xp + (((size_t)slot * a.T + t) * a.nb_d + b) * a.vx * 16);
   prep_pairs<FMT>(hi, pw, &nc_hi);
 #pragma unroll
-  for (int p = 0; p < 16; ++p) dst[p] = pw[p];
+  for (int v = 0; v < 4; ++v) dst[v] = uint4{pw[4 * v], pw[4 * v + 1], pw[4 * v + 2], pw[4 * v + 3]};
   if (a.vx == 2) {
     prep_pairs<FMT>(lo, pw, &nc_lo);
 #pragma unroll
-    for (int p = 0; p < 16; ++p) dst[16 + p] = pw[p];
+    for (int v = 0; v < 4; ++v)
+      dst[4 + v] = uint4{pw[4 * v], pw[4 * v + 1], pw[4 * v + 2], pw[4 * v + 3]};
   }
   a.xnc[((size_t)slot * a.nb_d + b) * a.T + t] = nc_hi + nc_lo;
 }
@@ -208,8 +225,10 @@ __global__ __launch_bounds__(256) void k_pf_prep(PfArgs a) {
   const int per_fmt = a.T * a.nb_d;
   const int nf = __builtin_popcount(a.gu_fmts);
   if (item >= nf * per_fmt) return;
+  // tokens fastest: the accumulator starts of neighbouring threads are
+  // neighbours ([slot][block][token])
   const int slot = item / per_fmt, rem = item % per_fmt;
-  const int t = rem / a.nb_d, b = rem % a.nb_d;
+  const int b = rem / a.T, t = rem % a.T;
   int fmt = 0;
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
     if (((a.gu_fmts >> f) & 1u) && a.fmt_slot[f] == slot) fmt = f;
@@ -242,15 +261,19 @@ __global__ __launch_bounds__(512) void k_pf_topk(PfArgs a) {
 // -------------------------------------------------------------- grouping
 
 // Entries (token, rank, weight) of expert blockIdx.x in token order: chunks
-// of 256 (token, rank) entries, compacted with a ballot per wave and the
-// wave counts through LDS.
-__global__ __launch_bounds__(256) void k_pf_group(PfArgs a) {
+// of kGroupThreads (token, rank) entries, compacted with a ballot per wave
+// and the wave counts through LDS (two count buffers, one barrier per
+// chunk); the ids of the next chunk are loaded while one is compacted.
+constexpr int kGroupThreads = 1024;
+constexpr int kGroupWaves = kGroupThreads / 64;
+
+__global__ __launch_bounds__(kGroupThreads) void k_pf_group(PfArgs a) {
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t *ltok = a.ltok + (size_t)e * a.T;
   int32_t *lrank = a.lrank + (size_t)e * a.T;
   float *lw = a.lw + (size_t)e * a.T;
   if (e == a.E) {  // the shared expert: every token, rank k, weight 1
-    for (int t = tid; t < a.T; t += 256) {
+    for (int t = tid; t < a.T; t += kGroupThreads) {
       ltok[t] = t;
       lrank[t] = a.k;
       lw[t] = 1.f;
@@ -258,21 +281,26 @@ __global__ __launch_bounds__(256) void k_pf_group(PfArgs a) {
     if (tid == 0) a.counts[e] = a.T;
     return;
   }
-  __shared__ int wcount[4];
+  __shared__ int wcount[2][kGroupWaves];
   int base = 0;
   const int n = a.T * a.k;
-  for (int j0 = 0; j0 < n; j0 += 256) {
+  int idn = tid < n ? a.ids[tid] : -1;
+  for (int j0 = 0, it = 0; j0 < n; j0 += kGroupThreads, ++it) {
     const int j = j0 + tid;
-    const bool hit = j < n && a.ids[j] == e;
+    const bool hit = idn == e;
+    const int jn = j + kGroupThreads;
+    idn = jn < n ? a.ids[jn] : -1;
     const uint64_t m = __ballot(hit);
     const int before = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wcount[wave] = __popcll(m);
+    int *wc = wcount[it & 1];
+    if (lane == 0) wc[wave] = __popcll(m);
     __syncthreads();
     int woff = 0, total = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (w < wave) woff += wcount[w];
-      total += wcount[w];
+    for (int w = 0; w < kGroupWaves; ++w) {
+      const int c = wc[w];
+      woff += w < wave ? c : 0;
+      total += c;
     }
     if (hit) {
       const int pos = base + woff + before;
@@ -281,7 +309,6 @@ __global__ __launch_bounds__(256) void k_pf_group(PfArgs a) {
       lw[pos] = a.gw[j];
     }
     base += total;
-    __syncthreads();
   }
   if (tid == 0) a.counts[e] = base;
 }
@@ -289,24 +316,55 @@ __global__ __launch_bounds__(256) void k_pf_group(PfArgs a) {
 // Row offsets (exclusive scan of the counts) and the task list.  One
 // workgroup of 1024 threads; experts e = tid, tid + 1024.
 __global__ __launch_bounds__(1024) void k_pf_plan(PfArgs a) {
-  __shared__ int cnt[1025], scan[1025], rem_rank_base[1];
-  const int tid = threadIdx.x, ne = a.E + 1;
+  __shared__ int cnt[1025], scan[1025], wsum[2][16], tot[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ne = a.E + 1;
   for (int e = tid; e < ne; e += 1024) cnt[e] = a.counts[e];
   __syncthreads();
-  if (tid == 0) {
-    // exclusive scans of rows and of full chunks (serial: at most 1025)
-    int rows = 0, full = 0;
-    for (int e = 0; e < ne; ++e) {
-      scan[e] = full;
-      a.offs[e] = rows;
-      rows += cnt[e];
-      full += cnt[e] / kChunk;
+  // exclusive scans of rows and of full chunks over the experts: thread i
+  // holds experts 2i and 2i + 1 (ne <= 1025 <= 2048); wave scans by lane
+  // shuffles, then the 16 wave totals
+  const int e0 = 2 * tid, e1 = 2 * tid + 1;
+  const int c0 = e0 < ne ? cnt[e0] : 0, c1 = e1 < ne ? cnt[e1] : 0;
+  const int own_r = c0 + c1, own_f = c0 / kChunk + c1 / kChunk;
+  int r = own_r, f = own_f;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int rr = __shfl_up(r, off, 64), ff = __shfl_up(f, off, 64);
+    if (lane >= off) {
+      r += rr;
+      f += ff;
     }
-    a.offs[ne] = rows;
-    rem_rank_base[0] = full;
+  }
+  if (lane == 63) {
+    wsum[0][wave] = r;
+    wsum[1][wave] = f;
   }
   __syncthreads();
-  const int nfull = rem_rank_base[0];
+  if (tid == 0) {
+    int sr = 0, sf = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int vr = wsum[0][w], vf = wsum[1][w];
+      wsum[0][w] = sr;
+      wsum[1][w] = sf;
+      sr += vr;
+      sf += vf;
+    }
+    tot[0] = sr;
+    tot[1] = sf;
+  }
+  __syncthreads();
+  const int rex = r - own_r + wsum[0][wave], fex = f - own_f + wsum[1][wave];
+  if (e0 < ne) {
+    a.offs[e0] = rex;
+    scan[e0] = fex;
+  }
+  if (e1 < ne) {
+    a.offs[e1] = rex + c0;
+    scan[e1] = fex + c0 / kChunk;
+  }
+  if (tid == 0) a.offs[ne] = tot[0];
+  __syncthreads();
+  const int nfull = tot[1];
   int nrem = 0;
   for (int e = 0; e < ne; ++e) nrem += (cnt[e] % kChunk) != 0;
   for (int e = tid; e < ne; e += 1024) {
@@ -1017,7 +1075,7 @@ hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, f
   const size_t nprep = (size_t)nf * T * a.nb_d;
   k_pf_prep<<<(unsigned)((nprep + 255) / 256), 256, 0, stream>>>(a);
   k_pf_topk<<<(T + 7) / 8, 512, 0, stream>>>(a);
-  k_pf_group<<<a.E + 1, 256, 0, stream>>>(a);
+  k_pf_group<<<a.E + 1, kGroupThreads, 0, stream>>>(a);
   k_pf_plan<<<1, 1024, 0, stream>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // workgroups: every task's slices, the tasks padded to a multiple of kXcds
