@@ -799,7 +799,7 @@ __device__ __forceinline__ void down_slot(const ExpArgs &a, const SlotCols &sc, 
 // rows, and the epilogue sums the waves in a fixed order, so y is the same
 // bit for bit from run to run.
 template <int G>
-__global__ __launch_bounds__(512) void k_down(ExpArgs a) {
+__global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_down(ExpArgs a) {
   __shared__ int32_t t_ncols[kMaxSlots];
   __shared__ int32_t t_cols[kMaxSlots][kQMax];
   __shared__ float t_w[kMaxSlots][kQMax];
