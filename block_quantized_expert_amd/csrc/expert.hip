@@ -584,63 +584,6 @@ __device__ __forceinline__ void lds_add(float *p, float v) {
   __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// One unit of one slot's down matrix for GP compact columns c0..: the
-// weighted row results are added into the wave's own accumulator rows
-// accw[column][row] (LDS, one writer lane per entry).
-template <int FMT, int GP, int R>
-__device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, int slot, int c0,
-                                          const Geo &geo, const UnitPos &up, int r0,
-                                          const MatPtr (&mats)[1], uint32_t cpitch,
-                                          uint32_t spitch, float *accw) {
-  using F = Fmt<FMT>;
-  const int lane = threadIdx.x & 63;
-  const int rg = lane / geo.lpr, li = lane % geo.lpr;
-  const int ch = li + geo.lpr * up.part;
-  const uint32_t coff = (uint32_t)(rg * cpitch + ch * F::CBYTES);
-  const uint32_t soff = (uint32_t)(rg * spitch + ch * F::SBYTES);
-  uint32_t cw[R][1][F::CW], sw[R][1];
-  unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + up.rloc_u, geo.rpi, coff, soff, cw, sw);
-  const uint32_t *hps = a.hp + (size_t)slot * a.q * a.nb_f * 32;
-  const float *hncs = a.hnc + (size_t)slot * a.q * a.nb_f;
-  uint32_t xr[GP][F::CB][2][16];
-  float ncr[GP][F::CB];
-  load_prepared_h<FMT, GP>(hps, hncs, a.nb_f, c0, ch, xr, ncr);
-  float to[R][1][GP];
-  unit_compute<FMT, GP, 2, 1, R>(cw, sw, xr, ncr, one_one_vgpr(), to);
-  const int rw = a.rw_dn;
-  int col[GP];
-  float wgt[GP];
-#pragma unroll
-  for (int g = 0; g < GP; ++g) {
-    col[g] = sc.col(c0 + g);
-    wgt[g] = sc.weight(c0 + g);
-  }
-  if (geo.lpr == 64) {  // one row per wave step: reduce all values at once
-    constexpr int N = R * GP;
-    float flat[N];
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int g = 0; g < GP; ++g) flat[i * GP + g] = to[i][0][g];
-    const float v = multi_sum<N>(flat, lane);
-    if (ms_writer<N>(lane)) {
-      const int n = ms_index<N>(lane);
-      const int i = n / GP, g = n % GP;
-      const int cg = (GP == 2 && g) ? col[GP - 1] : col[0];
-      const float wg = (GP == 2 && g) ? wgt[GP - 1] : wgt[0];
-      lds_add(&accw[cg * rw + up.rloc_u + i], wg * v);
-    }
-  } else {
-#pragma unroll
-    for (int g = 0; g < GP; ++g)
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const float v = group_sum(to[i][0][g], geo.lpr);
-        if (li == 0) lds_add(&accw[col[g] * rw + up.rloc_u + rg + geo.rpi * i], wgt[g] * v);
-      }
-  }
-}
-
 // Weighted row results of one computed down unit into the wave's
 // accumulator rows accw[column][row] (LDS, one writer lane per entry).  The
 // columns and weights come as separate scalars: a two-entry array indexed
@@ -675,6 +618,34 @@ __device__ __forceinline__ void down_reduce(const float (&to)[R][1][GP], const G
         if (li == 0) lds_add(&accw[(g ? col1 : col0) * rw + up.rloc_u + rg + geo.rpi * i], (g ? wgt1 : wgt0) * v);
       }
   }
+}
+
+// One unit of one slot's down matrix for GP compact columns c0..: the
+// weighted row results are added into the wave's own accumulator rows
+// accw[column][row] (LDS, one writer lane per entry).
+template <int FMT, int GP, int R>
+__device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, int slot, int c0,
+                                          const Geo &geo, const UnitPos &up, int r0,
+                                          const MatPtr (&mats)[1], uint32_t cpitch,
+                                          uint32_t spitch, float *accw) {
+  using F = Fmt<FMT>;
+  const int lane = threadIdx.x & 63;
+  const int rg = lane / geo.lpr, li = lane % geo.lpr;
+  const int ch = li + geo.lpr * up.part;
+  const uint32_t coff = (uint32_t)(rg * cpitch + ch * F::CBYTES);
+  const uint32_t soff = (uint32_t)(rg * spitch + ch * F::SBYTES);
+  uint32_t cw[R][1][F::CW], sw[R][1];
+  unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + up.rloc_u, geo.rpi, coff, soff, cw, sw);
+  const uint32_t *hps = a.hp + (size_t)slot * a.q * a.nb_f * 32;
+  const float *hncs = a.hnc + (size_t)slot * a.q * a.nb_f;
+  uint32_t xr[GP][F::CB][2][16];
+  float ncr[GP][F::CB];
+  load_prepared_h<FMT, GP>(hps, hncs, a.nb_f, c0, ch, xr, ncr);
+  float to[R][1][GP];
+  unit_compute<FMT, GP, 2, 1, R>(cw, sw, xr, ncr, one_one_vgpr(), to);
+  const int col0 = sc.col(c0), col1 = GP == 2 ? sc.col(c0 + GP - 1) : col0;
+  const float wgt0 = sc.weight(c0), wgt1 = GP == 2 ? sc.weight(c0 + GP - 1) : wgt0;
+  down_reduce<GP, R>(to, geo, up, a.rw_dn, col0, col1, wgt0, wgt1, accw);
 }
 
 // Units [u0, u1) of one slot's down matrix for GP compact columns c0..,
