@@ -11,14 +11,16 @@
 // "ROCmFPX": gate/up in FP2, down in FP3, the shared expert in FP4.
 //
 // Launches per step (after k_route, route.hip: router scores and prepared
-// activations):
+// activations; for steps of several columns also k_topk, which builds the
+// route table once):
 //   k_gateup  grid (f / RW_GU, slots).  Slot 0 is the shared expert (every
 //             column, weight 1): its workgroups need no routing and start
-//             streaming at once.  Workgroups of routed slots first run the
-//             routing step in LDS (sorted top-k, gating, slot table;
-//             deterministic, so all workgroups agree; rfpx_route.hpp) and
-//             workgroup (0, s) publishes slot s; then a gate/up tile of the
-//             slot's expert.
+//             streaming at once.  In a one-column step the workgroups of
+//             routed slots first run the routing step in LDS (sorted top-k
+//             and gating; deterministic, so all workgroups agree;
+//             rfpx_route.hpp) and workgroup (0, s) publishes slot s; in a
+//             step of several columns they copy their slot's entry of the
+//             route table.  Then a gate/up tile of the slot's expert.
 //   k_down    grid d / RW_DN.  A workgroup owns RW_DN rows of y for every
 //             column and runs the down rows of every slot into them, each
 //             row result times the column's gating weight: the combine is
@@ -30,8 +32,8 @@
 // issues every code and scale load of a unit up front (buffer loads: scalar
 // descriptor, scalar row offset, 32-bit lane offset), decodes each block in
 // registers once for all columns of the pass (v_dot2 on the prepared
-// pairs), reduces each row across its lanes with DPP and writes part sums to
-// LDS.  Then h = silu(g) * u, and the workgroup prepares h for the down
+// pairs), reduces each row across its lanes (DPP and permlane swaps) and
+// writes part sums to LDS.  Then h = silu(g) * u, and the workgroup prepares h for the down
 // matrix (bf16 hi + lo pair words) so k_down only loads it.
 // Lane geometry (Geo): with a row of >= 64 chunks a wave covers one row per
 // step and lane l reads chunk l (+ 64 for the second part; fully coalesced
