@@ -20,10 +20,11 @@ weight is re-read from the 256 MB last-level cache within a rotation.
 
 Timing: W warm-up steps, then K steps between two synchronizations, timed
 with events on the stream the kernels run on.  A second pass of K steps
-records a hipEvent between the three kernels of every step
-(moe_layer_forward_timed) to time the dominant kernel (the gate/up kernel)
-for the roofline entry.  The CPU oracle is timed on a bounded sample
-on the host.
+(moe_layer_forward_timed / moe_prefill_forward_timed) has every kernel of
+interest launched through hipExtLaunchKernel with a start and an end event,
+which the runtime stamps when that kernel starts and ends: the mean
+duration of the dominant kernel (the gate/up kernel) is the time of the
+roofline entry.  The CPU oracle is timed on a bounded sample on the host.
 
 Prints one JSON line.
 """
@@ -98,11 +99,12 @@ def expert_bytes(lay, e):
     return tot, gu
 
 
-KERNEL_SOURCES = ("expert.hip", "rfpx_impl.hpp", "rfpx_route.hpp", "abi.hip")
+KERNEL_SOURCES = ("expert.hip", "prefill.hip", "route.hip", "rfpx_impl.hpp", "rfpx_route.hpp",
+                  "abi.hip")
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the sources that define the decode kernels and their launch."""
+    """sha256 over the sources that define the layer kernels and their launch."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
@@ -135,6 +137,20 @@ def measured_traffic(kernel: str, workload: str):
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
+def calibration_copy(dev, mib):
+    """One plain fp32 copy kernel (torch.neg) of `mib` MiB, for scaling the
+    HBM byte counters of a profiled run."""
+    import torch
+    n = mib * (1 << 18)
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"# calibration copy: {4 * n} bytes read, {4 * n} bytes written",
+          file=sys.stderr, flush=True)
+
+
 def bench_prefill(args, cfg) -> int:
     """The 2048-token prefill chunk: moe_prefill_forward over layer images
     rotated so that no weight is re-read from the last-level cache."""
@@ -150,20 +166,38 @@ def bench_prefill(args, cfg) -> int:
     n_layers = args.layers or 2
     steps = min(args.steps, 40)
     warm = min(args.warmup, 4)
-    layers = []
+    layers, gu_bytes = [], []
     lay0 = x0_host = None
+    rows = cfg.q * (cfg.k + 1)
     for l in range(n_layers):
         lay = synth.gen_layer(cfg, l)
         L = bqe.upload_layer(lay)
         cols = synth.gen_columns(cfg, lay, cfg.q, layer=l)
         x = torch.from_numpy(cols.x.view(np.int16)).view(torch.bfloat16).to(dev)
-        layers.append((L, x, bqe.workspace(L, cfg.q, prefill=True)))
+        ws = bqe.workspace(L, cfg.q, prefill=True)
+        # the routing the chunk will take (8 columns per moe_route_topk call)
+        # must be the prescribed expert sets
+        rws = bqe.workspace(L, 8)
+        ids = np.concatenate([bqe.moe_route_topk(L, x[i:i + 8], ws=rws)[0].cpu().numpy()
+                              for i in range(0, cfg.q, 8)])
+        del rws
+        if cols.drawn is not None and not np.array_equal(ids, cols.drawn):
+            raise RuntimeError("routing differs from the prescribed expert sets")
+        # algorithmic bytes of the gate/up kernel: the packed gate/up blocks of
+        # every expert the chunk touches, the bf16 activations once, and h
+        # written once per (token, expert) row as bf16 hi + lo
+        touched = set(int(e) for e in ids.reshape(-1)) | {lay.E}
+        gu_bytes.append(sum(expert_bytes(lay, e)[1] for e in touched)
+                        + cfg.q * cfg.d * 2 + rows * cfg.f * 4)
+        layers.append((L, x, ws))
         weight_bytes = int(lay.blob.size)
         if l == 0 and args.cpu_seconds > 0:
             lay0, x0_host = lay, cols.x
         del lay
         print(f"# layer {l + 1}/{n_layers} ready", file=sys.stderr, flush=True)
     y = torch.empty((cfg.q, cfg.d), dtype=torch.float32, device=dev)
+    if args.calibrate_copy_mib > 0:
+        calibration_copy(dev, args.calibrate_copy_mib)
     for s in range(warm):
         L, x, ws = layers[s % n_layers]
         bqe.moe_prefill_forward(L, x, y=y, ws=ws)
@@ -177,8 +211,24 @@ def bench_prefill(args, cfg) -> int:
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / steps
-    rows = cfg.q * (cfg.k + 1)
     flops = 2.0 * rows * 3 * cfg.f * cfg.d  # gate, up and down of every (token, expert) row
+    gu_flops = 2.0 * rows * 2 * cfg.f * cfg.d  # gate and up only
+
+    # ---- timed pass: each stage's own kernel times
+    he = HipEvents()
+    evs = [he.create(6) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s, ev in enumerate(evs):
+        L, x, ws = layers[s % n_layers]
+        bqe.moe_prefill_forward_timed(L, x, y, ws, ev)
+    torch.cuda.synchronize()
+    st = {name: 1e3 * float(np.mean([he.elapsed_ms(ev[a], ev[b]) for ev in evs]))
+          for name, (a, b) in {"routing_and_grouping": (0, 1), "k_pf_gateup": (2, 3),
+                               "k_pf_down_and_combine": (4, 5),
+                               "first_start_to_last_end": (0, 5)}.items()}
+    for ev in evs:
+        he.destroy(ev)
+    gu_tflops = gu_flops / (st["k_pf_gateup"] * 1e-6) / 1e12
 
     # ---- CPU oracle on a bounded sample of the chunk: its first tokens, a
     # few at a time (each token is routed and computed on its own)
@@ -217,10 +267,14 @@ def bench_prefill(args, cfg) -> int:
                    "layers_rotated": n_layers, "seed_master": cfg.master},
         "useful_gflop": flops / 1e9,
         "mfma_utilization": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
-        "roofline": {"bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12,
+        "kernels_us": st,
+        "roofline": {"bound": "mfma", "achieved": gu_tflops,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
-                     "traffic": None, "kernel": "whole prefill chunk (all launches)"},
+                     "frac": gu_tflops / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("k_pf_gateup", cfg.name),
+                     "kernel": "k_pf_gateup (grouped gate/up product + SiLU gating)",
+                     "flops_per_launch": gu_flops,
+                     "bytes_per_launch": float(np.mean(gu_bytes))},
         "weight_GB_per_s": weight_bytes / (ms * 1e-3) / 1e9,
         "cpu_baseline": cpu,
     }
@@ -312,15 +366,7 @@ def main() -> int:
             bqe.moe_layer_forward_timed(L, x, y, ws, events)
 
     if args.calibrate_copy_mib > 0:
-        n = args.calibrate_copy_mib * (1 << 18)
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        print(f"# calibration copy: {4 * n} bytes read, {4 * n} bytes written",
-              file=sys.stderr, flush=True)
-        del src, dst
+        calibration_copy(dev, args.calibrate_copy_mib)
 
     for li, vi in warm:
         step(li, vi)
@@ -343,7 +389,7 @@ def main() -> int:
 
     # ---- timed pass: kernels of each step
     he = HipEvents()
-    evs = [he.create(4) for _ in order]
+    evs = [he.create(6) for _ in order]
     torch.cuda.synchronize()
     t0.record()
     for (li, vi), ev in zip(order, evs):
@@ -352,8 +398,9 @@ def main() -> int:
     torch.cuda.synchronize()
     total_ev_ms = t0.elapsed_time(t1)
     k_route = [he.elapsed_ms(ev[0], ev[1]) for ev in evs]
-    k_gu = [he.elapsed_ms(ev[1], ev[2]) for ev in evs]
-    k_dn = [he.elapsed_ms(ev[2], ev[3]) for ev in evs]
+    k_gu = [he.elapsed_ms(ev[2], ev[3]) for ev in evs]
+    k_dn = [he.elapsed_ms(ev[4], ev[5]) for ev in evs]
+    span = [he.elapsed_ms(ev[0], ev[5]) for ev in evs]
     for ev in evs:
         he.destroy(ev)
     gu_us = 1e3 * float(np.mean(k_gu))
@@ -412,11 +459,14 @@ def main() -> int:
             ("k_gateup (routing + gate/up of the shared and routed experts)" if cfg.q == 1 else
              "k_gateup (gate/up of the shared and routed experts)"): gu_us,
             "k_down (down of all slots + combine)": 1e3 * float(np.mean(k_dn)),
+            "first_start_to_last_end": 1e3 * float(np.mean(span)),
             "step_with_events": total_ev_ms * 1e3 / args.steps,
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_gateup (routing + gate/up dequant-GEMV + SiLU, shared and routed)",
+            "kernel": ("k_gateup (routing + gate/up dequant-GEMV + SiLU, shared and routed)"
+                       if cfg.q == 1 else
+                       "k_gateup (gate/up dequant-GEMV + SiLU, shared and routed)"),
             "achieved": gu_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -31,8 +31,8 @@ SYMBOLS = (
     "rfpx_block_bytes", "rfpx_matrix_bytes", "rfpx_pack", "rfpx_pack_codes",
     "rfpx_unpack", "moe_image_bytes", "moe_image_build", "moe_image_unpack",
     "moe_workspace_bytes", "moe_route_topk", "moe_layer_forward",
-    "moe_layer_forward_timed", "moe_prefill_forward", "rfpx_status_str",
-    "rfpx_last_error",
+    "moe_layer_forward_timed", "moe_prefill_forward", "moe_prefill_forward_timed",
+    "rfpx_status_str", "rfpx_last_error",
 )
 
 
@@ -89,6 +89,7 @@ def lib():
             "moe_layer_forward": (I, [LP, P, I, I, P, P, S, P]),
             "moe_layer_forward_timed": (I, [LP, P, I, I, P, P, S, P, P]),
             "moe_prefill_forward": (I, [LP, P, I, I, P, P, S, P]),
+            "moe_prefill_forward_timed": (I, [LP, P, I, I, P, P, S, P, P]),
             "rfpx_status_str": (C.c_char_p, [I]),
             "rfpx_last_error": (C.c_char_p, []),
         }
@@ -290,11 +291,12 @@ def moe_layer_forward(layer: MoeLayer, x, y=None, ws=None, stream=None):
 
 
 def moe_layer_forward_timed(layer: MoeLayer, x, y, ws, events, stream=None):
-    """events: a ctypes array of 4 hipEvent_t handles (created by the
-    caller on this device), recorded around the three kernels."""
+    """events: a ctypes array of 6 hipEvent_t handles (created by the
+    caller on this device), stamped with the start and end of the routing
+    kernels, the gate/up kernel and the down kernel."""
     _need_cuda(x)
-    if events is not None and len(events) != 4:
-        raise ValueError("moe_layer_forward_timed takes 4 events")
+    if events is not None and len(events) != 6:
+        raise ValueError("moe_layer_forward_timed takes 6 events")
     _check("moe_layer_forward_timed", lib().moe_layer_forward_timed(
         layer.ref, _ptr(x), _xtype(x), x.shape[0], _ptr(y), _ptr(ws), ws.numel(),
         _stream(stream), C.cast(events, C.c_void_p) if events is not None else None))
@@ -312,6 +314,21 @@ def moe_prefill_forward(layer: MoeLayer, x, y=None, ws=None, stream=None):
     _check("moe_prefill_forward", lib().moe_prefill_forward(
         layer.ref, _ptr(x), _xtype(x), T, _ptr(y), _ptr(ws), ws.numel(),
         _stream(stream)))
+    return y
+
+
+def moe_prefill_forward_timed(layer: MoeLayer, x, y, ws, events, stream=None):
+    """events: a ctypes array of 6 hipEvent_t handles (created by the
+    caller on this device), stamped with the start of the router scores, the
+    end of the expert grouping, the start and end of the grouped gate/up
+    product, the start of the grouped down product and the end of the
+    combine."""
+    _need_cuda(x)
+    if events is not None and len(events) != 6:
+        raise ValueError("moe_prefill_forward_timed takes 6 events")
+    _check("moe_prefill_forward_timed", lib().moe_prefill_forward_timed(
+        layer.ref, _ptr(x), _xtype(x), x.shape[0], _ptr(y), _ptr(ws), ws.numel(),
+        _stream(stream), C.cast(events, C.c_void_p) if events is not None else None))
     return y
 
 

@@ -266,16 +266,19 @@ rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x, int xtype
   p.ws = static_cast<uint8_t *>(ws);
   p.stream = (hipStream_t)stream;
   p.events = events;
-  hipEvent_t *ev = (hipEvent_t *)events;
-  hipError_t e = ev ? hipEventRecord(ev[0], p.stream) : hipSuccess;
-  if (e == hipSuccess) e = launch_route(p);
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], p.stream);
+  hipError_t e = launch_route(p);
   if (e == hipSuccess) e = launch_experts(p);
   return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_layer_forward: %s", hipGetErrorString(e));
 }
 
 rfpx_status moe_prefill_forward(const moe_layer *L, const void *x, int xtype, int T,
                                 float *y, void *ws, size_t ws_bytes, void *stream) {
+  return moe_prefill_forward_timed(L, x, xtype, T, y, ws, ws_bytes, stream, nullptr);
+}
+
+rfpx_status moe_prefill_forward_timed(const moe_layer *L, const void *x, int xtype, int T,
+                                      float *y, void *ws, size_t ws_bytes, void *stream,
+                                      void *const *events) {
   rfpx_status st = check_layer(L);
   if (st) return st;
   if (xtype != RFPX_X_F32 && xtype != RFPX_X_BF16) return fail(RFPX_E_ARG, "xtype=%d", xtype);
@@ -297,7 +300,7 @@ rfpx_status moe_prefill_forward(const moe_layer *L, const void *x, int xtype, in
   if (image_bytes > 0xFFFFFFFFull)
     return fail(RFPX_E_SHAPE, "prefill: image of %zu bytes exceeds 4 GiB", image_bytes);
   hipError_t e = launch_prefill(L, x, xtype, T, y, static_cast<uint8_t *>(ws), image_bytes,
-                                (hipStream_t)stream);
+                                (hipStream_t)stream, events);
   return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_prefill_forward: %s", hipGetErrorString(e));
 }
 

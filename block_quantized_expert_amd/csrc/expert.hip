@@ -896,21 +896,14 @@ hipError_t launch_experts(const ForwardPlan &p) {
   const unsigned nt = 64 * p.wmax, ntg = 64 * p.wgu;
   const bool bf = p.xtype == RFPX_X_BF16;
   hipEvent_t *ev = (hipEvent_t *)p.events;
-  if (p.g == 1) {
-    if (bf) k_gateup<1, 1><<<ggu, ntg, lds_gu, p.stream>>>(a);
-    else k_gateup<1, 2><<<ggu, ntg, lds_gu, p.stream>>>(a);
-  } else {
-    if (bf) k_gateup<2, 1><<<ggu, ntg, lds_gu, p.stream>>>(a);
-    else k_gateup<2, 2><<<ggu, ntg, lds_gu, p.stream>>>(a);
-  }
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], p.stream);
+  hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
+  void (*gu)(ExpArgs) = p.g == 1 ? (bf ? k_gateup<1, 1> : k_gateup<1, 2>)
+                                 : (bf ? k_gateup<2, 1> : k_gateup<2, 2>);
+  hipError_t e = launch_k(gu, ggu, dim3(ntg), lds_gu, p.stream, a, e0, e1);
   if (e != hipSuccess) return e;
-  if (p.g == 1) k_down<1><<<gdn, nt, lds_dn, p.stream>>>(a);
-  else k_down<2><<<gdn, nt, lds_dn, p.stream>>>(a);
-  e = hipGetLastError();
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[3], p.stream);
-  return e;
+  e0 = ev ? ev[4] : nullptr;
+  e1 = ev ? ev[5] : nullptr;
+  return launch_k(p.g == 1 ? k_down<1> : k_down<2>, gdn, dim3(nt), lds_dn, p.stream, a, e0, e1);
 }
 
 }  // namespace rfpx

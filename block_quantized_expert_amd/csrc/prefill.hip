@@ -1041,7 +1041,8 @@ size_t prefill_layout(const moe_layer *L, int T, int xtype, void *args_out) {
 }
 
 hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, float *y,
-                          uint8_t *ws, size_t image_bytes, hipStream_t stream) {
+                          uint8_t *ws, size_t image_bytes, hipStream_t stream,
+                          void *const *events) {
   PfArgs a;
   if (!prefill_layout(L, T, xtype, &a)) return hipErrorInvalidValue;
   // turn workspace offsets into pointers
@@ -1066,26 +1067,32 @@ hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, f
   a.wr = L->router_w;
   a.x = x;
   a.y = y;
+  hipEvent_t *ev = (hipEvent_t *)events;
+  auto evt = [ev](int i) { return ev ? ev[i] : nullptr; };
   const dim3 gsc((a.E + 63) / 64, (T + 31) / 32);
-  if (xtype == RFPX_X_BF16) k_pf_scores<RFPX_X_BF16><<<gsc, 256, 0, stream>>>(a);
-  else k_pf_scores<RFPX_X_F32><<<gsc, 256, 0, stream>>>(a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_k(xtype == RFPX_X_BF16 ? k_pf_scores<RFPX_X_BF16> : k_pf_scores<RFPX_X_F32>,
+                          gsc, dim3(256), 0, stream, a, evt(0));
   if (e != hipSuccess) return e;
   const int nf = __builtin_popcount(a.gu_fmts);
   const size_t nprep = (size_t)nf * T * a.nb_d;
-  k_pf_prep<<<(unsigned)((nprep + 255) / 256), 256, 0, stream>>>(a);
-  k_pf_topk<<<(T + 7) / 8, 512, 0, stream>>>(a);
-  k_pf_group<<<a.E + 1, kGroupThreads, 0, stream>>>(a);
-  k_pf_plan<<<1, 1024, 0, stream>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_k(k_pf_prep, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, stream,
+                    a)) != hipSuccess ||
+      (e = launch_k(k_pf_topk, dim3((T + 7) / 8), dim3(512), 0, stream, a)) != hipSuccess ||
+      (e = launch_k(k_pf_group, dim3(a.E + 1), dim3(kGroupThreads), 0, stream, a)) !=
+          hipSuccess ||
+      (e = launch_k(k_pf_plan, dim3(1), dim3(1024), 0, stream, a, nullptr, evt(1))) !=
+          hipSuccess)
+    return e;
   // workgroups: every task's slices, the tasks padded to a multiple of kXcds
   const int tpad = (a.max_tasks + kXcds - 1) / kXcds * kXcds;
   const int ggu = tpad * (a.f / kTileGU), gdn = tpad * (a.d / kTileDN);
-  if (a.vx == 1) k_pf_gateup<1><<<ggu, kPfThreads, 0, stream>>>(a);
-  else k_pf_gateup<2><<<ggu, kPfThreads, 0, stream>>>(a);
-  k_pf_down<<<gdn, kPfThreads, 0, stream>>>(a);
-  k_pf_combine<<<(unsigned)(((size_t)T * a.d / 4 + 255) / 256), 256, 0, stream>>>(a);
-  return hipGetLastError();
+  if ((e = launch_k(a.vx == 1 ? k_pf_gateup<1> : k_pf_gateup<2>, dim3(ggu), dim3(kPfThreads), 0,
+                    stream, a, evt(2), evt(3))) != hipSuccess ||
+      (e = launch_k(k_pf_down, dim3(gdn), dim3(kPfThreads), 0, stream, a, evt(4))) !=
+          hipSuccess)
+    return e;
+  return launch_k(k_pf_combine, dim3((unsigned)(((size_t)T * a.d / 4 + 255) / 256)), dim3(256),
+                  0, stream, a, nullptr, evt(5));
 }
 
 }  // namespace rfpx

@@ -543,6 +543,21 @@ size_t image_layout(int d, int f, int E, const int *fmts, ExpertDesc *desc);
 void set_error(const char *fmt, ...);
 rfpx_status fail(rfpx_status st, const char *fmt, ...);
 
+// Launch of a kernel that takes one argument struct.  With an event, the
+// launch goes through hipExtLaunchKernel, which stamps t0 with the time the
+// kernel starts and t1 with the time it ends (either may be null), so that
+// the interval between two stamps holds no launch gap; with neither, it is
+// an ordinary launch.
+template <typename A>
+inline hipError_t launch_k(void (*k)(A), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                           A a, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr) {
+  void *args[] = {&a};
+  if (!t0 && !t1)
+    return hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, lds, s);
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(k), grid, block, args, lds, s, t0,
+                            t1, 0);
+}
+
 // Launchers (route.hip, expert.hip).
 struct ForwardPlan {
   int d, f, E, k, q, xtype;
@@ -565,7 +580,9 @@ struct ForwardPlan {
   bool route_only;
   bool pre_route;           // the routing step runs once (k_topk) before the experts
   hipStream_t stream;
-  void *const *events;      // optional: 4 hipEvent_t recorded around launches
+  // optional, 6 hipEvent_t: start and end of the routing kernels, of the
+  // gate/up kernel and of the down kernel
+  void *const *events;
 };
 // k_route: router scores and prepared activations; for route_only and
 // pre_route also k_topk (the route table; ids and gating weights for
@@ -574,10 +591,12 @@ hipError_t launch_route(const ForwardPlan &p);
 // Prefill (prefill.hip): workspace bytes for T tokens (0: unsupported
 // shape); with args_out, also the kernel arguments with workspace offsets.
 size_t prefill_layout(const moe_layer *L, int T, int xtype, void *args_out);
+// events: null, or 6 hipEvent_t as for moe_prefill_forward_timed.
 hipError_t launch_prefill(const moe_layer *L, const void *x, int xtype, int T, float *y,
-                          uint8_t *ws, size_t image_bytes, hipStream_t stream);
-// k_gateup (all slots) and k_down (all slots, with the combine); records
-// events[2] and events[3] when events are given.
+                          uint8_t *ws, size_t image_bytes, hipStream_t stream,
+                          void *const *events);
+// k_gateup (all slots) and k_down (all slots, with the combine); stamps
+// events[2..5] when events are given.
 hipError_t launch_experts(const ForwardPlan &p);
 
 }  // namespace rfpx

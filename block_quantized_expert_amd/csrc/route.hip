@@ -189,17 +189,19 @@ hipError_t launch_route(const ForwardPlan &p) {
   a.xp = reinterpret_cast<uint32_t *>(p.ws + p.wl.xp);
   a.xnc = reinterpret_cast<float *>(p.ws + p.wl.xnc);
   const int n_prep_wg = (a.n_prep_items + kRouteThreads - 1) / kRouteThreads;
-  k_route<<<a.n_router_wg + n_prep_wg, kRouteThreads, 0, p.stream>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !(p.route_only || p.pre_route)) return e;
+  hipEvent_t *ev = (hipEvent_t *)p.events;
+  const bool topk = p.route_only || p.pre_route;
+  hipError_t e = launch_k(k_route, dim3(a.n_router_wg + n_prep_wg), dim3(kRouteThreads), 0,
+                          p.stream, a, ev ? ev[0] : nullptr, ev && !topk ? ev[1] : nullptr);
+  if (e != hipSuccess || !topk) return e;
   TopkArgs t{};
   t.rp = route_params(p);
   t.image = p.image;
   t.rt = reinterpret_cast<RouteTable *>(p.ws + p.wl.route);
   t.ids_out = p.ids_out;
   t.w_out = p.w_out;
-  k_topk<<<1, kTopkThreads, 0, p.stream>>>(t);
-  return hipGetLastError();
+  return launch_k(k_topk, dim3(1), dim3(kTopkThreads), 0, p.stream, t, nullptr,
+                  ev ? ev[1] : nullptr);
 }
 
 }  // namespace rfpx

@@ -180,12 +180,16 @@ rfpx_status moe_layer_forward(const moe_layer *L, const void *x_dev, int xtype,
                               int q, float *y_dev, void *ws_dev,
                               size_t ws_bytes, void *stream);
 
-/* moe_layer_forward that also records four caller-created hipEvent_t
- * handles on `stream`: events[0] before the first kernel (router scores and
- * prepared activations), events[1] after it, events[2] after the gate/up
- * kernel, events[3] after the down-and-combine kernel.  For measuring each
- * kernel of a step inside a timed loop; events may be NULL (then it is
- * moe_layer_forward).  The events must belong to the current device. */
+/* moe_layer_forward that also stamps six caller-created hipEvent_t handles
+ * (timing enabled, current device) with the start and end times of its
+ * kernels, as hipExtLaunchKernel does: events[0] when the router-score
+ * kernel starts, events[1] when the last routing kernel ends (the router
+ * scores, or the route table of a step of several columns), events[2] and
+ * events[3] when the gate/up kernel starts and ends, events[4] and events[5]
+ * when the down-and-combine kernel starts and ends.  hipEventElapsedTime of
+ * such a pair is the kernel's own duration, without launch gaps.  For
+ * measuring each kernel of a step inside a timed loop; events may be NULL
+ * (then it is moe_layer_forward). */
 rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x_dev,
                                     int xtype, int q, float *y_dev,
                                     void *ws_dev, size_t ws_bytes,
@@ -201,6 +205,18 @@ rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x_dev,
 rfpx_status moe_prefill_forward(const moe_layer *L, const void *x_dev,
                                 int xtype, int T, float *y_dev, void *ws_dev,
                                 size_t ws_bytes, void *stream);
+
+/* moe_prefill_forward that also stamps six caller-created hipEvent_t
+ * handles (timing enabled, current device) as moe_layer_forward_timed does:
+ * events[0] when the router-score kernel starts, events[1] when the
+ * expert-grouping kernels end, events[2] and events[3] when the grouped
+ * gate/up product starts and ends, events[4] when the grouped down product
+ * starts and events[5] when the combine kernel ends.  events may be NULL
+ * (then it is moe_prefill_forward). */
+rfpx_status moe_prefill_forward_timed(const moe_layer *L, const void *x_dev,
+                                      int xtype, int T, float *y_dev,
+                                      void *ws_dev, size_t ws_bytes,
+                                      void *stream, void *const *events);
 
 const char *rfpx_status_str(int status);
 const char *rfpx_last_error(void);

@@ -31,3 +31,53 @@ def to_device_x(cols_x):
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda")
     return torch.from_numpy(a.astype(np.float32)).to("cuda")
+
+
+class HipEvents:
+    """hipEvent_t handles (timing enabled) through the HIP runtime that torch
+    has loaded, for the *_timed entry points."""
+
+    def __init__(self):
+        import ctypes as C
+        path = None
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        assert path is not None, "HIP runtime not loaded"
+        self.C = C
+        self.lib = C.CDLL(path)
+        self.lib.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [C.c_void_p]
+
+    def create(self, n):
+        C = self.C
+        arr = (C.c_void_p * n)()
+        for i in range(n):
+            h = C.c_void_p()
+            assert self.lib.hipEventCreate(C.byref(h)) == 0
+            arr[i] = h
+        return arr
+
+    def ms(self, a, b) -> float:
+        out = self.C.c_float()
+        assert self.lib.hipEventElapsedTime(self.C.byref(out), a, b) == 0
+        return out.value
+
+    def destroy(self, arr):
+        for h in arr:
+            self.lib.hipEventDestroy(h)
+
+
+def check_stamps(he, ev):
+    """Six stamps of a *_timed call: three start/end intervals of positive
+    length, in launch order, inside the first-start-to-last-end span."""
+    d = [he.ms(ev[2 * i], ev[2 * i + 1]) for i in range(3)]
+    gaps = [he.ms(ev[1], ev[2]), he.ms(ev[3], ev[4])]
+    span = he.ms(ev[0], ev[5])
+    assert all(x > 0 for x in d), d
+    assert all(g >= -1e-3 for g in gaps), gaps
+    assert span >= sum(d) + sum(gaps) - 1e-3, (span, d, gaps)
+    return d

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     declared = header_functions()
-    assert len(declared) == 15
+    assert len(declared) == 16
     assert set(declared) == set(bqe.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name

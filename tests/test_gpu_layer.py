@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import assert_close, rel_err, to_device_x
+from gpu_common import HipEvents, assert_close, check_stamps, rel_err, to_device_x
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,29 @@ def test_tiny_bf16_activations(bqe, tiny):
     cols = synth.gen_columns(cfg16, lay, 4, variant=4)
     y_ref, _, _ = _oracle(lay, cols.x, "bf16")
     assert_close(_run(bqe, L, cols.x), y_ref, what="bf16 x")
+
+
+def test_timed_entry_point(bqe, tiny):
+    """moe_layer_forward_timed gives moe_layer_forward's output bit for bit
+    and stamps each kernel's start and end: one column (routing inside the
+    gate/up kernel) and three (a separate route-table kernel)."""
+    import torch
+    cfg, lay, L = tiny
+    he = HipEvents()
+    for q in (1, 3):
+        cols = synth.gen_columns(cfg, lay, q, variant=5)
+        x = to_device_x(cols.x)
+        ws = bqe.workspace(L, q)
+        y0 = bqe.moe_layer_forward(L, x, ws=ws)
+        y1 = torch.full_like(y0, float("nan"))
+        ev = he.create(6)
+        bqe.moe_layer_forward_timed(L, x, y1, ws, ev)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)
+        check_stamps(he, ev)
+        he.destroy(ev)
+    with pytest.raises(ValueError):
+        bqe.moe_layer_forward_timed(L, x, y1, ws, he.create(4))
 
 
 # ------------------------------------------------------- mixed small shapes

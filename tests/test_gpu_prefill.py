@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_common import assert_close, to_device_x
+from gpu_common import HipEvents, assert_close, check_stamps, to_device_x
 
 pytestmark = pytest.mark.gpu
 
@@ -114,6 +114,26 @@ def test_prefill_deterministic(bqe):
     c = synth.Config(**{**cfg.__dict__, "xtype": "bf16"})
     x = synth.gen_columns(c, lay, 170, variant=9).x
     assert np.array_equal(_prefill(bqe, L, x), _prefill(bqe, L, x))
+
+
+def test_prefill_timed_entry_point(bqe):
+    """moe_prefill_forward_timed gives moe_prefill_forward's output bit for
+    bit and stamps the stages' starts and ends in launch order."""
+    import torch
+    cfg, lay = _mixed_layer(512, 256, 16, 4, 6)
+    L = bqe.upload_layer(lay)
+    c = synth.Config(**{**cfg.__dict__, "xtype": "bf16"})
+    x = to_device_x(synth.gen_columns(c, lay, 150, variant=11).x)
+    ws = bqe.workspace(L, 150, prefill=True)
+    y0 = bqe.moe_prefill_forward(L, x, ws=ws)
+    y1 = torch.full_like(y0, float("nan"))
+    he = HipEvents()
+    ev = he.create(6)
+    bqe.moe_prefill_forward_timed(L, x, y1, ws, ev)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+    check_stamps(he, ev)
+    he.destroy(ev)
 
 
 def test_prefill_2048_tokens_zipf_sampled(bqe):
