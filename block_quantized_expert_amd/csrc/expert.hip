@@ -782,7 +782,9 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
   const int rw = a.rw_dn, q = a.q;
   const int waves = blockDim.x >> 6;
   const int wave = uniform(threadIdx.x >> 6);
-  const int nslots = uniform(a.rt->nslots);
+  // a one-column step always has k + 1 slots (k distinct experts), so its
+  // table loads need not wait for the slot count
+  const int nslots = G == 1 ? a.rp.k + 1 : uniform(a.rt->nslots);
   for (int i = threadIdx.x; i < waves * q * rw; i += blockDim.x) acc[i] = 0.f;
   // the slot table and each slot's down-matrix entry of the image table,
   // all loads in flight together
