@@ -110,6 +110,40 @@ def test_timed_entry_point(bqe, tiny):
         bqe.moe_layer_forward_timed(L, x, y1, ws, he.create(4))
 
 
+def test_graph_capture_replays(bqe, tiny):
+    """A decode step (one column, and three) captured in a HIP graph: the
+    library allocates nothing and issues no memset, so every replay gives
+    the eager result bit for bit, also with eager steps on other inputs
+    between the replays."""
+    import torch
+    cfg, lay, L = tiny
+    for q in (1, 3):
+        cols = synth.gen_columns(cfg, lay, 2 * q, variant=7)
+        x = to_device_x(cols.x[:q])
+        x_other = to_device_x(cols.x[q:])
+        ws = bqe.workspace(L, q)
+        y = torch.empty((q, cfg.d), dtype=torch.float32, device="cuda")
+        bqe.moe_layer_forward(L, x, y=y, ws=ws)
+        torch.cuda.synchronize()
+        y_eager = y.clone()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            bqe.moe_layer_forward(L, x, y=y, ws=ws)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            bqe.moe_layer_forward(L, x, y=y, ws=ws)
+        for _ in range(3):
+            y_other = bqe.moe_layer_forward(L, x_other, ws=ws)  # eager, same workspace
+            y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_eager), f"q={q}"
+            assert not torch.equal(y_other, y_eager)
+
+
 # ------------------------------------------------------- mixed small shapes
 
 @pytest.mark.parametrize("d,f,E,k,seed", [(512, 256, 16, 4, 1), (1024, 64, 32, 8, 2),
