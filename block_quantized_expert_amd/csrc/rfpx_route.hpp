@@ -58,10 +58,12 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 // units of an L2 would ask for the same lines, channel by channel, at the
 // same time).  Every load (the row and all Q columns of x) is issued before
 // the arithmetic, with clamped indices and zeroed after, so no load waits
-// on a branch or on another column's sums; the wave sums meet in LDS.
-template <int NT, int Q>
-__device__ __forceinline__ void router_row_q(const float *wr, const void *x, int xtype, int d,
-                                             int E, float *scores, int e) {
+// on a branch or on another column's sums; the wave sums meet in LDS.  The
+// activation type XT is a template argument: a run-time test around each
+// load made the compiler wait for every load before issuing the next.
+template <int NT, int Q, int XT>
+__device__ __forceinline__ void router_row_q(const float *wr, const void *x, int d, int E,
+                                             float *scores, int e) {
   constexpr int NPT = 4096 / 4 / NT;
   const int tid = threadIdx.x;
   const int n4 = d / 4;
@@ -83,7 +85,7 @@ __device__ __forceinline__ void router_row_q(const float *wr, const void *x, int
 #pragma unroll
     for (int j = 0; j < NPT; ++j) {
       const int i4 = idx[j];
-      if (xtype == RFPX_X_BF16) {
+      if constexpr (XT == RFPX_X_BF16) {
         const uint2 b = reinterpret_cast<const uint2 *>(
             static_cast<const uint16_t *>(x) + (size_t)c * d)[i4];
         xv[c][j] = make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
@@ -125,21 +127,28 @@ __device__ __forceinline__ void router_row_q(const float *wr, const void *x, int
   }
 }
 
-// router_row_q for a run-time column count q = 1..kQMax.
+// router_row_q for a run-time column count q = 1..kQMax and activation type.
+template <int NT, int XT>
+__device__ __forceinline__ void router_row_x(const float *wr, const void *x, int d, int E, int q,
+                                             float *scores, int e) {
+  static_assert(kQMax == 8, "one case per column count");
+  switch (q) {
+    case 1: router_row_q<NT, 1, XT>(wr, x, d, E, scores, e); break;
+    case 2: router_row_q<NT, 2, XT>(wr, x, d, E, scores, e); break;
+    case 3: router_row_q<NT, 3, XT>(wr, x, d, E, scores, e); break;
+    case 4: router_row_q<NT, 4, XT>(wr, x, d, E, scores, e); break;
+    case 5: router_row_q<NT, 5, XT>(wr, x, d, E, scores, e); break;
+    case 6: router_row_q<NT, 6, XT>(wr, x, d, E, scores, e); break;
+    case 7: router_row_q<NT, 7, XT>(wr, x, d, E, scores, e); break;
+    default: router_row_q<NT, 8, XT>(wr, x, d, E, scores, e); break;
+  }
+}
+
 template <int NT>
 __device__ __forceinline__ void router_row(const float *wr, const void *x, int xtype, int d,
                                            int E, int q, float *scores, int e) {
-  static_assert(kQMax == 8, "one case per column count");
-  switch (q) {
-    case 1: router_row_q<NT, 1>(wr, x, xtype, d, E, scores, e); break;
-    case 2: router_row_q<NT, 2>(wr, x, xtype, d, E, scores, e); break;
-    case 3: router_row_q<NT, 3>(wr, x, xtype, d, E, scores, e); break;
-    case 4: router_row_q<NT, 4>(wr, x, xtype, d, E, scores, e); break;
-    case 5: router_row_q<NT, 5>(wr, x, xtype, d, E, scores, e); break;
-    case 6: router_row_q<NT, 6>(wr, x, xtype, d, E, scores, e); break;
-    case 7: router_row_q<NT, 7>(wr, x, xtype, d, E, scores, e); break;
-    default: router_row_q<NT, 8>(wr, x, xtype, d, E, scores, e); break;
-  }
+  if (xtype == RFPX_X_BF16) router_row_x<NT, RFPX_X_BF16>(wr, x, d, E, q, scores, e);
+  else router_row_x<NT, RFPX_X_F32>(wr, x, d, E, q, scores, e);
 }
 
 // Order-preserving key of an fp32 score: larger score <=> larger key
