@@ -496,10 +496,9 @@ __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc
 // of 16 lanes).  LDS: hs [q][rw], then gup [2][2][q][rw].
 template <int G, int VX>
 __device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, int slot,
-                                          int tile, float *lds) {
+                                          int tile, float *lds, const ExpertDesc &ed) {
   float *hs = lds;
   float *gup = lds + a.q * a.rw_gu;
-  const ExpertDesc ed = load_desc(a.image, sc.expert);
   const int fmt = ed.fmt[0];
   if (fmt == RFPX_FP2) gateup_tile<RFPX_FP2, G, VX>(a, sc, ed, tile, hs, gup);
   else if (fmt == RFPX_FP3) gateup_tile<RFPX_FP3, G, VX>(a, sc, ed, tile, hs, gup);
@@ -535,6 +534,7 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
   __shared__ RouteLds rs;
   extern __shared__ float lds[];
   SlotCols sc;
+  ExpertDesc ed;
   if (slot == 0) {
     if (threadIdx.x < kQMax) {
       rs.cols[0][threadIdx.x] = threadIdx.x;
@@ -545,18 +545,32 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     sc.ncols = a.q;
     sc.cols = rs.cols[0];
     sc.w = rs.w[0];
+    ed = load_desc(a.image, a.rp.E);
   } else if (a.pre_routed) {
-    // the slot's entry of the route table, copied to LDS (the column list
-    // is then read through an LDS pointer on every path; a pointer that may
-    // be either LDS or global memory makes every read a slower flat access)
-    if (slot >= uniform(a.rt->nslots)) return;
+    // the slot's entry of the route table, planes included, every load
+    // issued before the slot count is tested (slot < max_slots, so the
+    // entry is inside the table); the column list is copied to LDS (it is
+    // then read through an LDS pointer on every path; a pointer that may be
+    // either LDS or global memory makes every read a slower flat access)
+    const int nslots = uniform(a.rt->nslots);
     sc.expert = uniform(a.rt->expert[slot]);
     sc.ncols = uniform(a.rt->ncols[slot]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      ed.codes[m] = uniform64(a.rt->gu_codes[slot][m]);
+      ed.scales[m] = uniform64(a.rt->gu_scales[slot][m]);
+      ed.fmt[m] = uniform(a.rt->gu_fmt[slot]);
+    }
+    ed.codes[2] = uniform64(a.rt->dn_codes[slot]);
+    ed.scales[2] = uniform64(a.rt->dn_scales[slot]);
+    ed.fmt[2] = uniform(a.rt->dn_fmt[slot]);
+    ed.reserved = 0;
     if (threadIdx.x < kQMax) {
       rs.cols[slot][threadIdx.x] = a.rt->cols[slot][threadIdx.x];
       rs.w[slot][threadIdx.x] = a.rt->w[slot][threadIdx.x];
     }
     __syncthreads();
+    if (slot >= nslots) return;
     sc.cols = rs.cols[slot];
     sc.w = rs.w[slot];
   } else {
@@ -573,8 +587,9 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     sc.ncols = uniform(rs.ncols[slot]);
     sc.cols = rs.cols[slot];
     sc.w = rs.w[slot];
+    ed = load_desc(a.image, sc.expert);
   }
-  gateup_wg<G, VX>(a, sc, slot, blockIdx.x, lds);
+  gateup_wg<G, VX>(a, sc, slot, blockIdx.x, lds, ed);
 }
 
 // ----------------------------------------------------------------- down

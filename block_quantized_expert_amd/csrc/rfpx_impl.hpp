@@ -135,6 +135,11 @@ struct RouteTable {
   uint64_t dn_codes[kMaxSlots];
   uint64_t dn_scales[kMaxSlots];
   int32_t dn_fmt[kMaxSlots];
+  // and its gate and up planes (steps of several columns), so that a gate/up
+  // workgroup finds everything it needs in one round of loads
+  uint64_t gu_codes[kMaxSlots][2];
+  uint64_t gu_scales[kMaxSlots][2];
+  int32_t gu_fmt[kMaxSlots];
 };
 
 struct WsLayout {

@@ -121,36 +121,41 @@ struct TopkArgs {
 constexpr int kTopkThreads = 512;
 constexpr int kTopkDescPerThread = (kEMax + 1 + kTopkThreads - 1) / kTopkThreads;
 
+// The image-table fields of one expert that the expert kernels read: every
+// plane offset and the gate/up and down formats.
+struct SlotPlanes {
+  uint64_t codes[3], scales[3];
+  int32_t fmt_gu, fmt_dn;
+};
+
 __global__ __launch_bounds__(kTopkThreads) void k_topk(TopkArgs a) {
   __shared__ RouteLds s;
-  __shared__ uint64_t dn_codes[kEMax + 1], dn_scales[kEMax + 1];
-  __shared__ int32_t dn_fmt[kEMax + 1];
+  __shared__ SlotPlanes planes[kEMax + 1];
   __shared__ uint32_t scr[2 * kEMax];
   const int tid = threadIdx.x;
   const int q = a.rp.q, k = a.rp.k, E = a.rp.E;
-  // the down-matrix entries of the image table (shared expert included),
-  // loaded before the routing step so they arrive with the scores
+  // the image-table entries (shared expert included), loaded before the
+  // routing step so they arrive with the scores
   const ExpertDesc *tab = a.image ? reinterpret_cast<const ExpertDesc *>(a.image + kImgTable) : nullptr;
-  uint64_t pc[kTopkDescPerThread], ps[kTopkDescPerThread];
-  int32_t pf[kTopkDescPerThread];
+  SlotPlanes pp[kTopkDescPerThread];
 #pragma unroll
   for (int i = 0; i < kTopkDescPerThread; ++i) {
     const int e = tid + kTopkThreads * i;
     if (tab && e <= E) {
-      pc[i] = tab[e].codes[2];
-      ps[i] = tab[e].scales[2];
-      pf[i] = tab[e].fmt[2];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) {
+        pp[i].codes[m] = tab[e].codes[m];
+        pp[i].scales[m] = tab[e].scales[m];
+      }
+      pp[i].fmt_gu = tab[e].fmt[0];
+      pp[i].fmt_dn = tab[e].fmt[2];
     }
   }
   route_wg(a.rp, &s, scr);
 #pragma unroll
   for (int i = 0; i < kTopkDescPerThread; ++i) {
     const int e = tid + kTopkThreads * i;
-    if (tab && e <= E) {
-      dn_codes[e] = pc[i];
-      dn_scales[e] = ps[i];
-      dn_fmt[e] = pf[i];
-    }
+    if (tab && e <= E) planes[e] = pp[i];
   }
   if (a.ids_out)
     for (int i = tid; i < q * k; i += blockDim.x) {
@@ -161,10 +166,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk(TopkArgs a) {
   publish_route(s, q, -1, true, a.rt);  // the whole table
   __syncthreads();
   if (tab && tid < s.nslots) {
-    const int e = s.expert[tid];
-    a.rt->dn_codes[tid] = dn_codes[e];
-    a.rt->dn_scales[tid] = dn_scales[e];
-    a.rt->dn_fmt[tid] = dn_fmt[e];
+    const SlotPlanes &sp = planes[s.expert[tid]];
+    a.rt->dn_codes[tid] = sp.codes[2];
+    a.rt->dn_scales[tid] = sp.scales[2];
+    a.rt->dn_fmt[tid] = sp.fmt_dn;
+    a.rt->gu_codes[tid][0] = sp.codes[0];
+    a.rt->gu_codes[tid][1] = sp.codes[1];
+    a.rt->gu_scales[tid][0] = sp.scales[0];
+    a.rt->gu_scales[tid][1] = sp.scales[1];
+    a.rt->gu_fmt[tid] = sp.fmt_gu;
   }
 }
 
