@@ -141,7 +141,7 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   p->g = q == 1 ? 1 : 2;
   // with several columns the routing step costs more and every routed
   // gate/up workgroup would repeat it: run it once before the experts
-  p->pre_route = q > 1;
+  p->pre_route = q > 1;  // exactly the steps of two-column passes (g = 2)
   // waves per down workgroup (a multiple of the column parts, 1 or 2)
   p->wmax = q == 1 ? kDnWavesQ1 : kDnWavesQn;
   // gate/up workgroups: waves and the smallest tile; a wave streams

@@ -54,7 +54,6 @@ struct ExpArgs {
   float *y;
   int d, f, q, nb_d, nb_f;
   int rw_gu, rw_dn;
-  int pre_routed;  // the route table is complete before the launch
   Geo geo_gu[5], geo_dn[5];
 };
 
@@ -496,9 +495,11 @@ __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc
 // of 16 lanes).  LDS: hs [q][rw], then gup [2][2][q][rw].
 template <int G, int VX>
 __device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, int slot,
-                                          int tile, float *lds, const ExpertDesc &ed) {
+                                          int tile, float *lds, const ExpertDesc *pre) {
   float *hs = lds;
   float *gup = lds + a.q * a.rw_gu;
+  // the expert's planes: from the route table when given, else the image
+  const ExpertDesc ed = pre ? *pre : load_desc(a.image, sc.expert);
   const int fmt = ed.fmt[0];
   if (fmt == RFPX_FP2) gateup_tile<RFPX_FP2, G, VX>(a, sc, ed, tile, hs, gup);
   else if (fmt == RFPX_FP3) gateup_tile<RFPX_FP3, G, VX>(a, sc, ed, tile, hs, gup);
@@ -525,16 +526,16 @@ __device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, 
 }
 
 // Gate/up tile blockIdx.x of slot blockIdx.y.  Slot 0 is the shared expert
-// (every column, weight 1, no routing); routed slots read their entry of
-// the route table when it was built before the launch, else run the
-// routing step in LDS first.
+// (every column, weight 1, no routing).  Routed slots of a step of several
+// columns (G = 2) read their entry of the route table, which k_topk built
+// before the launch; those of a one-column step (G = 1) run the routing
+// step in LDS first.
 template <int G, int VX>
 __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
   const int slot = blockIdx.y;
   __shared__ RouteLds rs;
   extern __shared__ float lds[];
   SlotCols sc;
-  ExpertDesc ed;
   if (slot == 0) {
     if (threadIdx.x < kQMax) {
       rs.cols[0][threadIdx.x] = threadIdx.x;
@@ -545,16 +546,17 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     sc.ncols = a.q;
     sc.cols = rs.cols[0];
     sc.w = rs.w[0];
-    ed = load_desc(a.image, a.rp.E);
-  } else if (a.pre_routed) {
-    // the slot's entry of the route table, planes included, every load
-    // issued before the slot count is tested (slot < max_slots, so the
-    // entry is inside the table); the column list is copied to LDS (it is
-    // then read through an LDS pointer on every path; a pointer that may be
-    // either LDS or global memory makes every read a slower flat access)
+  } else if constexpr (G == 2) {
+    // steps of several columns are routed before the launch: the slot's
+    // entry of the route table, planes included, every load issued before
+    // the slot count is tested (slot < max_slots, so the entry is inside
+    // the table); the column list is copied to LDS (it is then read through
+    // an LDS pointer on every path; a pointer that may be either LDS or
+    // global memory makes every read a slower flat access)
     const int nslots = uniform(a.rt->nslots);
     sc.expert = uniform(a.rt->expert[slot]);
     sc.ncols = uniform(a.rt->ncols[slot]);
+    ExpertDesc ed;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       ed.codes[m] = uniform64(a.rt->gu_codes[slot][m]);
@@ -573,9 +575,10 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     if (slot >= nslots) return;
     sc.cols = rs.cols[slot];
     sc.w = rs.w[slot];
+    gateup_wg<G, VX>(a, sc, slot, blockIdx.x, lds, &ed);
+    return;
   } else {
     // one-column step: routing in the workgroup, slot s is rank s - 1
-    // (steps of several columns are always routed before the launch)
     route_q1(a.rp, &rs, slot);
     if (slot >= uniform(rs.nslots)) return;
     if (blockIdx.x == 0) {
@@ -587,9 +590,8 @@ __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
     sc.ncols = uniform(rs.ncols[slot]);
     sc.cols = rs.cols[slot];
     sc.w = rs.w[slot];
-    ed = load_desc(a.image, sc.expert);
   }
-  gateup_wg<G, VX>(a, sc, slot, blockIdx.x, lds, ed);
+  gateup_wg<G, VX>(a, sc, slot, blockIdx.x, lds, nullptr);
 }
 
 // ----------------------------------------------------------------- down
@@ -899,7 +901,6 @@ ExpArgs make_args(const ForwardPlan &p) {
   }
   a.rw_gu = p.rw_gu;
   a.rw_dn = p.rw_dn;
-  a.pre_routed = p.pre_route ? 1 : 0;
   return a;
 }
 
