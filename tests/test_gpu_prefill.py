@@ -158,3 +158,28 @@ def test_prefill_2048_tokens_zipf_sampled(bqe):
         assert_close(y[t:t + 1], yd.cpu().numpy(), tol=1e-4, what=f"decode vs prefill token {t}")
     del L
     torch.cuda.empty_cache()
+
+
+def test_prefill_max_tokens(bqe):
+    """The largest chunk the entry point accepts (T = 65536) on the tiny
+    layer: the busiest experts get over a thousand 64-row tasks.  64 tokens
+    spread over the chunk against the oracle, 16 against the decode path,
+    and every output finite."""
+    import torch
+    cfg = synth.Config(**{**synth.WORKLOADS[synth.TINY].__dict__, "xtype": "bf16"})
+    lay = synth.gen_layer(cfg, 0, threads=4)
+    L = bqe.upload_layer(lay)
+    T = 65536
+    cols = synth.gen_columns(cfg, lay, T, variant=13)
+    y = _prefill(bqe, L, cols.x)
+    assert y.shape == (T, cfg.d) and np.all(np.isfinite(y))
+    rng = np.random.default_rng(13)
+    sample = sorted(set(rng.choice(T, 62, replace=False).tolist()) | {0, T - 1})
+    assert_close(y[sample], _oracle_rows(lay, cols.x, "bf16", sample), what="sampled tokens")
+    xd = to_device_x(cols.x)
+    for t in rng.choice(T, 16, replace=False).tolist():
+        yd = bqe.moe_layer_forward(L, xd[t:t + 1])
+        torch.cuda.synchronize()
+        assert_close(y[t:t + 1], yd.cpu().numpy(), tol=1e-4, what=f"decode vs prefill token {t}")
+    del L, xd
+    torch.cuda.empty_cache()
