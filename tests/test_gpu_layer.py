@@ -242,3 +242,22 @@ def test_verify_q5_hot_fp4(bqe, layer):
     assert_close(y, np.concatenate(refs), what=f"layer {layer}")
     del L
     torch.cuda.empty_cache()
+
+
+def test_decode_max_shape(bqe):
+    """d = f = 4096 (the largest of both), k = 8 and q = 8 (the largest)
+    together, bf16 and fp32 activations: every column against the oracle."""
+    import torch
+    cfg = synth.Config("maxshape", 4096, 4096, 16, 8, 8, "bf16", "natural", scale_floor=1e-3,
+                       master=777)
+    lay = synth.gen_layer(cfg, 0, threads=8)
+    L = bqe.upload_layer(lay)
+    for xt in ("bf16", "f32"):
+        c2 = synth.Config(**{**cfg.__dict__, "xtype": xt})
+        cols = synth.gen_columns(c2, lay, 8, variant=1)
+        y = _run(bqe, L, cols.x)
+        with cf.ThreadPoolExecutor(8) as ex:
+            refs = list(ex.map(lambda c: _oracle(lay, cols.x[c:c + 1], xt)[0], range(8)))
+        assert_close(y, np.concatenate(refs), what=f"{xt} q=8")
+    del L
+    torch.cuda.empty_cache()
