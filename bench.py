@@ -24,7 +24,10 @@ with events on the stream the kernels run on.  A second pass of K steps
 interest launched through hipExtLaunchKernel with a start and an end event,
 which the runtime stamps when that kernel starts and ends: the mean
 duration of the dominant kernel (the gate/up kernel) is the time of the
-roofline entry.  The CPU oracle is timed on a bounded sample on the host.
+roofline entry.  Stamped launches leave wider gaps between the kernels, so
+that pass gives kernel durations only ("kernels_us"; its whole-step figures
+are longer than a step); value and ms_per_step come from the first pass.
+The CPU oracle is timed on a bounded sample on the host.
 
 Prints one JSON line.
 """
