@@ -28,10 +28,14 @@ BLOCK_BYTES = {RFPX_FP2: 10, RFPX_FP3: 14, RFPX_FP4: 17}
 
 # every symbol include/rfpx.h declares
 SYMBOLS = (
-    "rfpx_block_bytes", "rfpx_matrix_bytes", "rfpx_pack", "rfpx_pack_codes",
-    "rfpx_unpack", "moe_image_bytes", "moe_image_build", "moe_image_unpack",
+    "rfpx_block_bytes", "rfpx_matrix_bytes", "rfpx_pack", "rfpx_pack_weighted",
+    "rfpx_pack_codes",
+    "rfpx_unpack", "moe_image_bytes", "moe_image_build", "moe_image_validate",
+    "moe_image_unpack",
     "moe_workspace_bytes", "moe_route_topk", "moe_layer_forward",
     "moe_layer_forward_timed", "moe_prefill_forward", "moe_prefill_forward_timed",
+    "rfpx_dense_image_bytes", "rfpx_dense_image_build", "rfpx_dense_image_unpack",
+    "rfpx_dense_workspace_bytes", "rfpx_dense_forward",
     "rfpx_status_str", "rfpx_last_error",
 )
 
@@ -46,7 +50,7 @@ class MoeLayerC(C.Structure):
     _fields_ = [("d", C.c_int), ("f", C.c_int), ("n_experts", C.c_int),
                 ("top_k", C.c_int), ("routed_scale", C.c_float),
                 ("router_w", C.c_void_p), ("image", C.c_void_p),
-                ("fmts", C.POINTER(C.c_int))]
+                ("fmts", C.POINTER(C.c_int)), ("image_bytes", C.c_size_t)]
 
 
 _lock = threading.Lock()
@@ -79,10 +83,12 @@ def lib():
             "rfpx_block_bytes": (S, [I]),
             "rfpx_matrix_bytes": (S, [I, I, I]),
             "rfpx_pack": (I, [I, P, I, I, P, S, P]),
+            "rfpx_pack_weighted": (I, [I, P, P, I, I, P, S, P]),
             "rfpx_pack_codes": (I, [I, P, P, I, I, P, S, P]),
             "rfpx_unpack": (I, [I, P, I, I, P, P]),
             "moe_image_bytes": (S, [I, I, I, P]),
             "moe_image_build": (I, [I, I, I, P, P, P, S, P]),
+            "moe_image_validate": (I, [LP, P, P]),
             "moe_image_unpack": (I, [LP, I, I, P, P]),
             "moe_workspace_bytes": (S, [LP, I, I]),
             "moe_route_topk": (I, [LP, P, I, I, P, P, P, S, P]),
@@ -90,6 +96,11 @@ def lib():
             "moe_layer_forward_timed": (I, [LP, P, I, I, P, P, S, P, P]),
             "moe_prefill_forward": (I, [LP, P, I, I, P, P, S, P]),
             "moe_prefill_forward_timed": (I, [LP, P, I, I, P, P, S, P, P]),
+            "rfpx_dense_image_bytes": (S, [I, I, I]),
+            "rfpx_dense_image_build": (I, [I, P, I, I, P, S, P]),
+            "rfpx_dense_image_unpack": (I, [I, P, I, I, P, P]),
+            "rfpx_dense_workspace_bytes": (S, [I, I, I, I]),
+            "rfpx_dense_forward": (I, [I, P, I, I, P, I, I, P, P, S, P]),
             "rfpx_status_str": (C.c_char_p, [I]),
             "rfpx_last_error": (C.c_char_p, []),
         }
@@ -145,6 +156,22 @@ def rfpx_pack(fmt: int, w, out=None, stream=None):
         out = torch.empty(n, dtype=torch.uint8, device=w.device)
     _check("rfpx_pack", lib().rfpx_pack(fmt, _ptr(w), rows, cols, _ptr(out),
                                         out.numel(), _stream(stream)))
+    return out
+
+
+def rfpx_pack_weighted(fmt: int, w, imp, out=None, stream=None):
+    """Importance-weighted quantizer: w cuda fp32 [rows][cols], imp cuda
+    fp32 [cols] (>= 0)."""
+    import torch
+    _need_cuda(w, imp)
+    rows, cols = w.shape
+    if imp.numel() != cols:
+        raise ValueError("imp must hold one importance per column")
+    n = rfpx_matrix_bytes(fmt, rows, cols)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w.device)
+    _check("rfpx_pack_weighted", lib().rfpx_pack_weighted(
+        fmt, _ptr(w), _ptr(imp), rows, cols, _ptr(out), out.numel(), _stream(stream)))
     return out
 
 
@@ -206,22 +233,52 @@ def moe_image_build(d: int, f: int, n_experts: int, fmts,
 
 class MoeLayer:
     """A layer descriptor (moe_layer) plus references that keep its device
-    buffers and format table alive."""
+    buffers and format table alive.  image_bytes defaults to the size of
+    the image tensor."""
 
     def __init__(self, d: int, f: int, n_experts: int, top_k: int, router_w,
-                 image, fmts, routed_scale: float = 1.0):
+                 image, fmts, routed_scale: float = 1.0,
+                 image_bytes: Optional[int] = None):
         _need_cuda(router_w, image)
         self._fmts = _fmts_array(fmts)
         self._router_w = router_w
         self._image = image
+        if image_bytes is None:
+            image_bytes = image.numel()
         self.c = MoeLayerC(d, f, n_experts, top_k, routed_scale,
                            router_w.data_ptr(), image.data_ptr(),
-                           C.cast(self._fmts, C.POINTER(C.c_int)))
+                           C.cast(self._fmts, C.POINTER(C.c_int)), image_bytes)
         self.d, self.f, self.n_experts, self.top_k = d, f, n_experts, top_k
 
     @property
     def ref(self):
         return C.byref(self.c)
+
+
+def moe_image_validate(layer: MoeLayer, report=None, stream=None):
+    """Enqueue the device check of the layer's image; returns the report
+    tensor (cuda int32 [4], read as uint32: header faults, mismatching table
+    entries, blocks with a non-finite scale, 0), valid once the stream
+    passes."""
+    import torch
+    if report is None:
+        report = torch.empty(4, dtype=torch.int32, device=layer._image.device)
+    _need_cuda(report)
+    _check("moe_image_validate", lib().moe_image_validate(layer.ref, _ptr(report),
+                                                          _stream(stream)))
+    return report
+
+
+def check_image(layer: MoeLayer, stream=None) -> None:
+    """moe_image_validate, waited for: raises RfpxError if the image fails."""
+    import torch
+    rep = moe_image_validate(layer, stream=stream)
+    (stream or torch.cuda.current_stream()).synchronize()
+    r = [int(v) & 0xFFFFFFFF for v in rep.cpu().tolist()]
+    if any(r):
+        raise RfpxError("moe_image_validate", -4,
+                        f"header faults 0x{r[0]:x}, {r[1]} table entries differ from the "
+                        f"format table, {r[2]} blocks with a non-finite scale")
 
 
 def moe_image_unpack(layer: MoeLayer, expert: int, matrix: int, out=None,
@@ -332,12 +389,63 @@ def moe_prefill_forward_timed(layer: MoeLayer, x, y, ws, events, stream=None):
     return y
 
 
+# ------------------------------------------------------ dense projections
+
+class DenseMatrix:
+    """A dense block-quantized matrix in its device image (rows x cols,
+    format fmt), built from canonical blocks by rfpx_dense_image_build."""
+
+    def __init__(self, fmt: int, rows: int, cols: int, canonical, stream=None):
+        import torch
+        _need_cuda(canonical)
+        n = lib().rfpx_dense_image_bytes(fmt, rows, cols)
+        if n == 0:
+            raise RfpxError("rfpx_dense_image_bytes", -2, f"unsupported {rows} x {cols}")
+        self.image = torch.empty(n, dtype=torch.uint8, device=canonical.device)
+        _check("rfpx_dense_image_build", lib().rfpx_dense_image_build(
+            fmt, _ptr(canonical), rows, cols, _ptr(self.image), n, _stream(stream)))
+        self.fmt, self.rows, self.cols = fmt, rows, cols
+
+    def unpack(self, out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty((self.rows, self.cols), dtype=torch.float32,
+                              device=self.image.device)
+        _check("rfpx_dense_image_unpack", lib().rfpx_dense_image_unpack(
+            self.fmt, _ptr(self.image), self.rows, self.cols, _ptr(out), _stream(stream)))
+        return out
+
+    def workspace(self, q: int):
+        import torch
+        n = lib().rfpx_dense_workspace_bytes(self.fmt, self.rows, self.cols, q)
+        if n == 0:
+            raise RfpxError("rfpx_dense_workspace_bytes", -2, "unsupported shape")
+        return torch.empty(n, dtype=torch.uint8, device=self.image.device)
+
+
+def rfpx_dense_forward(m: DenseMatrix, x, y=None, ws=None, stream=None):
+    """y[q][rows] = W x_c for the q columns of x (cuda bf16 or fp32
+    [q][cols])."""
+    import torch
+    _need_cuda(x)
+    q = x.shape[0]
+    if y is None:
+        y = torch.empty((q, m.rows), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = m.workspace(q)
+    _check("rfpx_dense_forward", lib().rfpx_dense_forward(
+        m.fmt, _ptr(m.image), m.rows, m.cols, _ptr(x), _xtype(x), q, _ptr(y), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return y
+
+
 # ----------------------------------------------------------- convenience
 
-def upload_layer(lay, device="cuda", stream=None) -> MoeLayer:
+def upload_layer(lay, device="cuda", stream=None, validate: bool = True) -> MoeLayer:
     """Build the device image of a synthetic layer (an object with d, f, E,
     k, wr, fmts, blob, offsets, mat(e, m)): one host-to-device copy of all
-    canonical bytes, then moe_image_build on the GPU."""
+    canonical bytes, then moe_image_build on the GPU, then (by default)
+    moe_image_validate, raising if the image fails it."""
     import numpy as np
     import torch
     blob = torch.from_numpy(np.ascontiguousarray(lay.blob)).to(device)
@@ -351,6 +459,9 @@ def upload_layer(lay, device="cuda", stream=None) -> MoeLayer:
     wr = torch.from_numpy(np.ascontiguousarray(lay.wr)).to(device)
     L = MoeLayer(lay.d, lay.f, lay.E, lay.k, wr, image, lay.fmts,
                  getattr(lay, "routed_scale", 1.0))
-    torch.cuda.current_stream().synchronize()  # canonical bytes freed after this
+    if validate:
+        check_image(L)  # waits for the stream, so the canonical bytes may go
+    else:
+        torch.cuda.current_stream().synchronize()
     del blob, canon
     return L

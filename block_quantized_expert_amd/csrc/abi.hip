@@ -10,9 +10,11 @@
 #include <stdio.h>
 #include <string.h>
 
+
 #include "rfpx_impl.hpp"
 
 namespace rfpx {
+
 
 static thread_local char g_err[512];
 
@@ -87,6 +89,8 @@ bool pick_tile_down(const Geo *geo, unsigned fmts, int g, int rows, int min_rows
   return true;
 }
 
+}  // namespace
+
 rfpx_status check_layer(const moe_layer *L) {
   if (!L) return fail(RFPX_E_ARG, "layer is null");
   if (!L->fmts) return fail(RFPX_E_ARG, "layer format table is null");
@@ -106,6 +110,18 @@ rfpx_status check_layer(const moe_layer *L) {
       return fail(RFPX_E_FORMAT, "expert %d: gate and up formats differ", e);
   return RFPX_OK;
 }
+
+rfpx_status check_image(const moe_layer *L) {
+  if (!L->image) return fail(RFPX_E_ARG, "layer image is null");
+  if ((uintptr_t)L->image % 256) return fail(RFPX_E_ALIGN, "image not 256-byte aligned");
+  const size_t need = image_layout(L->d, L->f, L->n_experts, L->fmts, nullptr);
+  if (L->image_bytes != need)
+    return fail(RFPX_E_FORMAT, "image_bytes is %zu, the format table lays out %zu", L->image_bytes,
+                need);
+  return RFPX_OK;
+}
+
+namespace {
 
 // Everything a decode step needs that depends only on shapes and formats.
 rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
@@ -184,15 +200,25 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   return RFPX_OK;
 }
 
-rfpx_status check_run(const moe_layer *L, const ForwardPlan &p, const void *x,
-                      void *ws, size_t ws_bytes) {
-  if (!L->router_w || !L->image) return fail(RFPX_E_ARG, "layer router or image is null");
+// Router, image and activations of a decode call; the image is checked only
+// when the call reads it (moe_route_topk does not).
+rfpx_status check_inputs(const moe_layer *L, const void *x, bool reads_image) {
+  if (!L->router_w) return fail(RFPX_E_ARG, "layer router is null");
+  rfpx_status st = reads_image ? check_image(L) : RFPX_OK;
+  if (st) return st;
   if (!x) return fail(RFPX_E_ARG, "x is null");
-  if (!ws) return fail(RFPX_E_ARG, "workspace is null");
-  if ((uintptr_t)ws % 256) return fail(RFPX_E_ALIGN, "workspace not 256-byte aligned");
-  if ((uintptr_t)L->image % 256) return fail(RFPX_E_ALIGN, "image not 256-byte aligned");
   if ((uintptr_t)L->router_w % 16 || (uintptr_t)x % 16)
     return fail(RFPX_E_ALIGN, "router weights and x must be 16-byte aligned");
+  return RFPX_OK;
+}
+
+// ... and the workspace.
+rfpx_status check_run(const moe_layer *L, const ForwardPlan &p, const void *x,
+                      void *ws, size_t ws_bytes, bool reads_image) {
+  rfpx_status st = check_inputs(L, x, reads_image);
+  if (st) return st;
+  if (!ws) return fail(RFPX_E_ARG, "workspace is null");
+  if ((uintptr_t)ws % 256) return fail(RFPX_E_ALIGN, "workspace not 256-byte aligned");
   if (ws_bytes < p.wl.total)
     return fail(RFPX_E_WORKSPACE, "workspace holds %zu bytes, needs %zu", ws_bytes, p.wl.total);
   return RFPX_OK;
@@ -236,7 +262,7 @@ rfpx_status moe_route_topk(const moe_layer *L, const void *x, int xtype, int q,
   ForwardPlan p;
   rfpx_status st = make_plan(L, q, xtype, &p);
   if (st) return st;
-  if ((st = check_run(L, p, x, ws, ws_bytes))) return st;
+  if ((st = check_run(L, p, x, ws, ws_bytes, false))) return st;
   if (!ids || !w) return fail(RFPX_E_ARG, "ids or w is null");
   p.x = x;
   p.ids_out = ids;
@@ -259,7 +285,7 @@ rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x, int xtype
   ForwardPlan p;
   rfpx_status st = make_plan(L, q, xtype, &p);
   if (st) return st;
-  if ((st = check_run(L, p, x, ws, ws_bytes))) return st;
+  if ((st = check_run(L, p, x, ws, ws_bytes, true))) return st;
   if (!y) return fail(RFPX_E_ARG, "y is null");
   p.x = x;
   p.y = y;
@@ -288,15 +314,15 @@ rfpx_status moe_prefill_forward_timed(const moe_layer *L, const void *x, int xty
                 L->d, L->f);
   const size_t need = prefill_layout(L, T, xtype, nullptr);
   if (!need) return fail(RFPX_E_SHAPE, "prefill: unsupported shape (T=%d)", T);
-  if (!L->router_w || !L->image) return fail(RFPX_E_ARG, "layer router or image is null");
+  if (!L->router_w) return fail(RFPX_E_ARG, "layer router is null");
+  if ((st = check_image(L))) return st;
   if (!x || !y || !ws) return fail(RFPX_E_ARG, "x, y or workspace is null");
   if ((uintptr_t)ws % 256) return fail(RFPX_E_ALIGN, "workspace not 256-byte aligned");
-  if ((uintptr_t)L->image % 256) return fail(RFPX_E_ALIGN, "image not 256-byte aligned");
   if ((uintptr_t)L->router_w % 16 || (uintptr_t)x % 16 || (uintptr_t)y % 16)
     return fail(RFPX_E_ALIGN, "router weights, x and y must be 16-byte aligned");
   if (ws_bytes < need)
     return fail(RFPX_E_WORKSPACE, "workspace holds %zu bytes, needs %zu", ws_bytes, need);
-  const size_t image_bytes = image_layout(L->d, L->f, L->n_experts, L->fmts, nullptr);
+  const size_t image_bytes = L->image_bytes;
   if (image_bytes > 0xFFFFFFFFull)
     return fail(RFPX_E_SHAPE, "prefill: image of %zu bytes exceeds 4 GiB", image_bytes);
   hipError_t e = launch_prefill(L, x, xtype, T, y, static_cast<uint8_t *>(ws), image_bytes,

@@ -139,6 +139,109 @@ __global__ __launch_bounds__(kThreads) void k_pack(const float *__restrict__ w,
   write_block<FMT>(dst, c, s16);
 }
 
+// Importance-weighted quantizer (page "DeepSeek V4 Flash 在 128GB 锐龙 AI
+// MAX+ 上跑到 32 tok/s", section "ROCmFPX": weights are quantized with an
+// importance matrix).  Per block: candidate scales around the absmax one
+// (FP2/FP3: fp16 of a / (o t), t = 1, 1 + 1/16, 1 - 1/16, ..., 1 +- 8/16;
+// FP4: exponents e0, e0 - 1, e0 + 1), nearest codes from each stored scale,
+// and the candidate of least sum_j imp_j (w_j - (c_j - o) s)^2 is kept (the
+// first listed on a tie).  The error is a decision: it is evaluated in
+// double with every operation rounded on its own (no fused multiply-add),
+// in column order, so that the choice is reproducible bit for bit.
+#pragma clang fp contract(off)
+template <int FMT>
+__device__ inline double wblock_error(const float *v, const float *imp, const int *c,
+                                      double s) {
+  constexpr double O = FMT == RFPX_FP2 ? 1.5 : FMT == RFPX_FP3 ? 3.5 : 7.5;
+  double err = 0.0;
+  for (int j = 0; j < 32; ++j) {
+    const double d = (double)v[j] - ((double)c[j] - O) * s;
+    err = err + (double)imp[j] * (d * d);
+  }
+  return err;
+}
+
+template <int FMT>
+__device__ inline void wblock_codes(const float *v, double s, int *c) {
+  constexpr double O = FMT == RFPX_FP2 ? 1.5 : FMT == RFPX_FP3 ? 3.5 : 7.5;
+  constexpr double CMAX = (double)((1 << FMT) - 1);
+  for (int j = 0; j < 32; ++j) c[j] = (int)fmin(fmax(rint((double)v[j] / s + O), 0.0), CMAX);
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_pack_weighted(const float *__restrict__ w,
+                                                            const float *__restrict__ imp,
+                                                            int nb, long long nblk,
+                                                            uint8_t *__restrict__ out) {
+  long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= nblk) return;
+  constexpr int BB = blk_bytes(FMT);
+  constexpr double O = FMT == RFPX_FP2 ? 1.5 : FMT == RFPX_FP3 ? 3.5 : 7.5;
+  const float *src = w + i * 32;
+  const float *im = imp + (i % nb) * 32;  // the block's 32 input columns
+  float v[32], a = 0.f;
+  for (int j = 0; j < 32; ++j) {
+    v[j] = src[j];
+    a = fmaxf(a, fabsf(v[j]));
+  }
+  uint8_t *dst = out + i * BB;
+  int c[32], best_c[32];
+  double best = 0.0;
+  bool have = false;
+  uint32_t best_bits = 0;
+  if (a != 0.f) {
+    if (FMT == RFPX_FP4) {
+      const int e0 = 127 + ceil_log2_pos((double)a / O);
+      int seen[3], nseen = 0;
+      for (int k = 0; k < 3; ++k) {
+        int e = k == 0 ? e0 : k == 1 ? e0 - 1 : e0 + 1;
+        e = e < 1 ? 1 : (e > 254 ? 254 : e);
+        bool dup = false;
+        for (int n = 0; n < nseen; ++n) dup |= seen[n] == e;
+        if (dup) continue;
+        seen[nseen++] = e;
+        const double sc = ldexp(1.0, e - 127);
+        wblock_codes<FMT>(v, sc, c);
+        const double err = wblock_error<FMT>(v, im, c, sc);
+        if (!have || err < best) {
+          have = true;
+          best = err;
+          best_bits = (uint32_t)e;
+          for (int j = 0; j < 32; ++j) best_c[j] = c[j];
+        }
+      }
+    } else {
+      uint16_t seen[17];
+      int nseen = 0;
+      for (int k = 0; k < 17; ++k) {
+        const int t = (k + 1) / 2 * ((k & 1) ? 1 : -1);  // 0, 1, -1, 2, -2, ...
+        uint16_t s16 = dbl_to_half_rne((double)a / (O * (1.0 + (double)t / 16.0)));
+        if ((s16 & 0x7FFFu) == 0x7C00u) s16 = 0x7BFF;
+        const double sc = (double)half_bits_to_float(s16);
+        if (sc == 0.0) continue;
+        bool dup = false;
+        for (int n = 0; n < nseen; ++n) dup |= seen[n] == s16;
+        if (dup) continue;
+        seen[nseen++] = s16;
+        wblock_codes<FMT>(v, sc, c);
+        const double err = wblock_error<FMT>(v, im, c, sc);
+        if (!have || err < best) {
+          have = true;
+          best = err;
+          best_bits = s16;
+          for (int j = 0; j < 32; ++j) best_c[j] = c[j];
+        }
+      }
+    }
+  }
+  if (!have) {
+    for (int j = 0; j < BB; ++j) dst[j] = 0;
+    return;
+  }
+  write_block<FMT>(dst, best_c, best_bits);
+}
+#pragma clang fp contract(fast)
+
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void k_pack_codes(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ sbits,
@@ -200,6 +303,125 @@ __global__ __launch_bounds__(kThreads) void k_image_matrix(
   for (int j = 0; j < sb; ++j) sc[j] = s[cb + j];
 }
 
+// ------------------------------------------------------------ validation
+// The host format table travels in the kernel arguments, two bits per
+// matrix (format - 2): 3 (E + 1) <= 3075 entries fit in 193 words.
+constexpr int kFmtWords = (3 * (kEMax + 1) * 2 + 31) / 32;
+
+struct ValArgs {
+  const uint8_t *image;
+  uint32_t *report;
+  size_t image_bytes;
+  int d, f, E;
+  uint32_t fmt_bits[kFmtWords];
+};
+
+__device__ __forceinline__ int val_fmt(const ValArgs &a, int i) {
+  return RFPX_FP2 + (int)((a.fmt_bits[i >> 4] >> (2 * (i & 15))) & 3u);
+}
+
+// Bytes entry i = 3 e + m of the layout occupies: its codes plane and its
+// scales plane, each rounded up to 256 bytes (the layout of image_layout).
+__device__ __forceinline__ uint64_t val_entry_bytes(const ValArgs &a, int i) {
+  const int fmt = val_fmt(a, i), m = i % 3;
+  const uint64_t rows = m < 2 ? a.f : a.d, cols = m < 2 ? a.d : a.f;
+  const uint64_t nblk = rows * (cols / 32);
+  return align_up(nblk * code_bytes(fmt), 256) + align_up(nblk * scale_bytes(fmt), 256);
+}
+
+// Start of entry i (its codes plane) in the layout of the host table: the
+// table's aligned end plus the bytes of entries 0..i-1, summed by the
+// workgroup.  All threads must call it; it ends with a barrier.
+__device__ uint64_t val_entry_start(const ValArgs &a, int i, uint64_t *red) {
+  uint64_t part = 0;
+  for (int j = threadIdx.x; j < i; j += blockDim.x) part += val_entry_bytes(a, j);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+  __syncthreads();
+  uint64_t tot = align_up(kImgTable + (uint64_t)(a.E + 1) * sizeof(ExpertDesc), 256);
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
+  __syncthreads();
+  return tot;
+}
+
+// Header and expert table (one workgroup): report[0] header faults,
+// report[1] mismatching table entries; clears report[2], report[3] for the
+// scale scan that follows on the same stream.  Each thread walks a
+// contiguous run of entries, starting from the sum of the runs below it.
+__global__ __launch_bounds__(kThreads) void k_validate_head(ValArgs a) {
+  __shared__ uint64_t run_bytes[kThreads];
+  __shared__ uint32_t bad;
+  const int tid = threadIdx.x, n = 3 * (a.E + 1);
+  const int per = (n + kThreads - 1) / kThreads, i0 = tid * per, i1 = min(n, i0 + per);
+  uint64_t mine = 0;
+  for (int i = i0; i < i1; ++i) mine += val_entry_bytes(a, i);
+  run_bytes[tid] = mine;
+  if (tid == 0) bad = 0;
+  __syncthreads();
+  uint64_t off = align_up(kImgTable + (uint64_t)(a.E + 1) * sizeof(ExpertDesc), 256);
+  for (int t = 0; t < tid; ++t) off += run_bytes[t];
+  const ExpertDesc *tab = reinterpret_cast<const ExpertDesc *>(a.image + kImgTable);
+  uint32_t mis = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int e = i / 3, m = i % 3, fmt = val_fmt(a, i);
+    const uint64_t rows = m < 2 ? a.f : a.d, cols = m < 2 ? a.d : a.f;
+    const uint64_t codes = off, scales = align_up(off + rows * (cols / 32) * code_bytes(fmt), 256);
+    if (tab[e].fmt[m] != fmt || tab[e].codes[m] != codes || tab[e].scales[m] != scales) ++mis;
+    off += val_entry_bytes(a, i);
+  }
+  if (mis) atomicAdd(&bad, mis);
+  __syncthreads();
+  if (tid == 0) {
+    const ImageHeader *h = reinterpret_cast<const ImageHeader *>(a.image);
+    uint32_t hf = 0;
+    if (h->magic != kMagic) hf |= 1u;
+    if (h->version != kVersion) hf |= 2u;
+    if (h->d != a.d || h->f != a.f || h->E != a.E) hf |= 4u;
+    if (h->total != a.image_bytes) hf |= 8u;
+    a.report[0] = hf;
+    a.report[1] = bad;
+    a.report[2] = 0;
+    a.report[3] = 0;
+  }
+}
+
+// Scales of entry blockIdx.y (at the offset the host table implies), part
+// blockIdx.x of gridDim.x: counts fp16 Inf/NaN (FP2/FP3) or E8M0 = 255
+// (FP4) into report[2].  Planes are 256-byte aligned and read as words;
+// the tail past the last whole word is read bytewise.
+__global__ __launch_bounds__(kThreads) void k_validate_scales(ValArgs a) {
+  __shared__ uint64_t red[kThreads / 64];
+  const int i = blockIdx.y, fmt = val_fmt(a, i), m = i % 3;
+  const uint64_t rows = m < 2 ? a.f : a.d, cols = m < 2 ? a.d : a.f;
+  const uint64_t nblk = rows * (cols / 32);
+  const uint64_t start = val_entry_start(a, i, red);
+  const uint8_t *sp = a.image + align_up(start + nblk * code_bytes(fmt), 256);
+  const uint64_t nbytes = nblk * scale_bytes(fmt), nwords = nbytes / 4;
+  const uint32_t *w = reinterpret_cast<const uint32_t *>(sp);
+  uint32_t cnt = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * kThreads;
+  for (uint64_t j = (uint64_t)blockIdx.x * kThreads + threadIdx.x; j < nwords; j += stride) {
+    const uint32_t v = w[j];
+    if (fmt == RFPX_FP4) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) cnt += ((v >> (8 * b)) & 0xFFu) == 0xFFu;
+    } else {
+      cnt += (v & 0x7C00u) == 0x7C00u;
+      cnt += (v & 0x7C000000u) == 0x7C000000u;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    for (uint64_t b = nwords * 4; b < nbytes; b += scale_bytes(fmt)) {
+      if (fmt == RFPX_FP4) cnt += sp[b] == 0xFFu;
+      else cnt += ((sp[b] | (sp[b + 1] << 8)) & 0x7C00) == 0x7C00;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+  if ((threadIdx.x & 63) == 0 && cnt) atomicAdd(&a.report[2], cnt);
+}
+
 unsigned grid_for(long long n) { return (unsigned)((n + kThreads - 1) / kThreads); }
 
 rfpx_status check_matrix(int fmt, int rows, int cols) {
@@ -244,6 +466,27 @@ rfpx_status rfpx_pack(int fmt, const float *w, int rows, int cols, uint8_t *out,
   }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "rfpx_pack: %s", hipGetErrorString(e));
+}
+
+rfpx_status rfpx_pack_weighted(int fmt, const float *w, const float *imp, int rows, int cols,
+                               uint8_t *out, size_t cap, void *stream) {
+  rfpx_status st = check_matrix(fmt, rows, cols);
+  if (st) return st;
+  long long nblk = (long long)rows * (cols / 32);
+  if (nblk == 0) return RFPX_OK;
+  if (!w || !imp || !out) return fail(RFPX_E_ARG, "rfpx_pack_weighted: null pointer");
+  if (cap < rfpx_matrix_bytes(fmt, rows, cols))
+    return fail(RFPX_E_WORKSPACE, "rfpx_pack_weighted: output holds %zu bytes, needs %zu", cap,
+                rfpx_matrix_bytes(fmt, rows, cols));
+  hipStream_t s = (hipStream_t)stream;
+  const int nb = cols / 32;
+  switch (fmt) {
+    case RFPX_FP2: k_pack_weighted<RFPX_FP2><<<grid_for(nblk), kThreads, 0, s>>>(w, imp, nb, nblk, out); break;
+    case RFPX_FP3: k_pack_weighted<RFPX_FP3><<<grid_for(nblk), kThreads, 0, s>>>(w, imp, nb, nblk, out); break;
+    default: k_pack_weighted<RFPX_FP4><<<grid_for(nblk), kThreads, 0, s>>>(w, imp, nb, nblk, out); break;
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "rfpx_pack_weighted: %s", hipGetErrorString(e));
 }
 
 rfpx_status rfpx_pack_codes(int fmt, const uint8_t *codes, const uint16_t *sbits,
@@ -329,13 +572,39 @@ rfpx_status moe_image_build(int d, int f, int n_experts, const int *fmts,
   return err == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_image_build: %s", hipGetErrorString(err));
 }
 
+rfpx_status moe_image_validate(const moe_layer *L, uint32_t *report, void *stream) {
+  rfpx_status st = check_layer(L);
+  if (st) return st;
+  if ((st = check_image(L))) return st;
+  if (!report) return fail(RFPX_E_ARG, "moe_image_validate: report is null");
+  if ((uintptr_t)report % 4) return fail(RFPX_E_ALIGN, "moe_image_validate: report not 4-byte aligned");
+  ValArgs a{};
+  a.image = L->image;
+  a.report = report;
+  a.image_bytes = L->image_bytes;
+  a.d = L->d;
+  a.f = L->f;
+  a.E = L->n_experts;
+  const int n = 3 * (L->n_experts + 1);
+  for (int i = 0; i < n; ++i)
+    a.fmt_bits[i >> 4] |= (uint32_t)(L->fmts[i] - RFPX_FP2) << (2 * (i & 15));
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_k(k_validate_head, dim3(1), dim3(kThreads), 0, s, a);
+  // enough parts per plane that the scan spreads over the device
+  const int parts = n >= 512 ? 4 : n >= 64 ? 16 : 64;
+  if (e == hipSuccess)
+    e = launch_k(k_validate_scales, dim3(parts, n), dim3(kThreads), 0, s, a);
+  return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_image_validate: %s", hipGetErrorString(e));
+}
+
 rfpx_status moe_image_unpack(const moe_layer *L, int expert, int matrix, float *w,
                              void *stream) {
-  if (!L || !L->fmts || !L->image || !w) return fail(RFPX_E_ARG, "moe_image_unpack: null pointer");
+  rfpx_status st = check_layer(L);
+  if (st) return st;
+  if ((st = check_image(L))) return st;
+  if (!w) return fail(RFPX_E_ARG, "moe_image_unpack: null pointer");
   if (expert < 0 || expert > L->n_experts || matrix < 0 || matrix > 2)
     return fail(RFPX_E_ARG, "moe_image_unpack: expert %d matrix %d out of range", expert, matrix);
-  if (!moe_image_bytes(L->d, L->f, L->n_experts, L->fmts))
-    return fail(RFPX_E_SHAPE, "moe_image_unpack: bad layer shape or format table");
   ExpertDesc *desc = new ExpertDesc[L->n_experts + 1];
   image_layout(L->d, L->f, L->n_experts, L->fmts, desc);
   int fmt = L->fmts[3 * expert + matrix];

@@ -54,8 +54,17 @@ struct ExpArgs {
   float *y;
   int d, f, q, nb_d, nb_f;
   int rw_gu, rw_dn;
-  Geo geo_gu[5], geo_dn[5];
+  Geo geo_gu[5], geo_dn[5];  // by format; all zero for a format not in the host table
 };
+
+// A format read from the device table that the launch was planned for: the
+// plan fills the geometry of exactly the formats of the host table (the
+// arrays are indexed by constants only, so they stay in scalar registers).
+__device__ __forceinline__ bool planned(const Geo (&geo)[5], int fmt) {
+  return fmt == RFPX_FP2 ? geo[RFPX_FP2].cpl != 0
+       : fmt == RFPX_FP3 ? geo[RFPX_FP3].cpl != 0
+       : fmt == RFPX_FP4 ? geo[RFPX_FP4].cpl != 0 : false;
+}
 
 // The columns of one slot: expert and count in scalar registers; the column
 // list and weights stay in LDS and are read when a pass needs them (indexing
@@ -501,6 +510,7 @@ __device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, 
   // the expert's planes: from the route table when given, else the image
   const ExpertDesc ed = pre ? *pre : load_desc(a.image, sc.expert);
   const int fmt = ed.fmt[0];
+  if (!planned(a.geo_gu, fmt)) return;  // a table that disagrees with fmts
   if (fmt == RFPX_FP2) gateup_tile<RFPX_FP2, G, VX>(a, sc, ed, tile, hs, gup);
   else if (fmt == RFPX_FP3) gateup_tile<RFPX_FP3, G, VX>(a, sc, ed, tile, hs, gup);
   else gateup_tile<RFPX_FP4, G, VX>(a, sc, ed, tile, hs, gup);
@@ -811,7 +821,10 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
       t_ncols[s] = a.rt->ncols[s];
       t_codes[s] = a.rt->dn_codes[s];
       t_scales[s] = a.rt->dn_scales[s];
-      t_fmt[s] = a.rt->dn_fmt[s];
+      // a format the launch was not planned for (a device table that
+      // disagrees with the host table) becomes 0: the slot is skipped
+      const int f = a.rt->dn_fmt[s];
+      t_fmt[s] = planned(a.geo_dn, f) ? f : 0;
     } else {
       t_cols[s][j] = a.rt->cols[s][j];
       t_w[s][j] = a.rt->w[s][j];
@@ -830,7 +843,9 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
   const int ups2 = rw / (unit_rows_for(RFPX_FP2, G) * a.geo_dn[RFPX_FP2].rpi);
   const int ups3 = rw / (unit_rows_for(RFPX_FP3, G) * a.geo_dn[RFPX_FP3].rpi);
   const int ups4 = rw / (unit_rows_for(RFPX_FP4, G) * a.geo_dn[RFPX_FP4].rpi);
-  auto slot_units = [&](int fmt) { return fmt == RFPX_FP2 ? ups2 : fmt == RFPX_FP3 ? ups3 : ups4; };
+  auto slot_units = [&](int fmt) {
+    return fmt == RFPX_FP2 ? ups2 : fmt == RFPX_FP3 ? ups3 : fmt == RFPX_FP4 ? ups4 : 0;
+  };
   if (runs) {
     int total = 0;
     for (int s = 0; s < nslots; ++s) total += slot_units(uniform(t_fmt[s]));
@@ -869,7 +884,7 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
     const int fmt = uniform(t_fmt[s]);
     if (fmt == RFPX_FP2) down_slot<RFPX_FP2, G>(a, sc, s, ed, r0, wave, waves, item, accw);
     else if (fmt == RFPX_FP3) down_slot<RFPX_FP3, G>(a, sc, s, ed, r0, wave, waves, item, accw);
-    else down_slot<RFPX_FP4, G>(a, sc, s, ed, r0, wave, waves, item, accw);
+    else if (fmt == RFPX_FP4) down_slot<RFPX_FP4, G>(a, sc, s, ed, r0, wave, waves, item, accw);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < q * rw; i += blockDim.x) {

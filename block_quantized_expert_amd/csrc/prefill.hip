@@ -66,7 +66,7 @@ struct PfArgs {
   int d, f, E, k, T, xtype, vx, nb_d, nb_f;
   float routed_scale;
   int rows_max, max_tasks;
-  unsigned gu_fmts;
+  unsigned gu_fmts, dn_fmts;  // bit f: format f appears in the host table
   int fmt_slot[5];
   // workspace
   float *scores;       // [T][E]
@@ -865,6 +865,9 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(PfArgs a) {
   __shared__ __align__(16) PfLds sm;
   const ExpertDesc ed = pf_desc(a, tk.expert);
   const int fmt = ed.fmt[0];
+  // a device table that disagrees with the host table: no activations were
+  // prepared for an unplanned format
+  if (fmt < 0 || fmt > 4 || !((a.gu_fmts >> fmt) & 1u)) return;
   if (fmt == RFPX_FP2) pf_gateup_task<RFPX_FP2, VX>(a, tk, ed, slice, sm);
   else if (fmt == RFPX_FP3) pf_gateup_task<RFPX_FP3, VX>(a, tk, ed, slice, sm);
   else pf_gateup_task<RFPX_FP4, VX>(a, tk, ed, slice, sm);
@@ -934,6 +937,7 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(PfArgs a) {
   __shared__ __align__(16) PfLds sm;
   const ExpertDesc ed = pf_desc(a, tk.expert);
   const int fmt = ed.fmt[2];
+  if (fmt < 0 || fmt > 4 || !((a.dn_fmts >> fmt) & 1u)) return;
   if (fmt == RFPX_FP2) pf_down_task<RFPX_FP2>(a, tk, ed, slice, sm);
   else if (fmt == RFPX_FP3) pf_down_task<RFPX_FP3>(a, tk, ed, slice, sm);
   else pf_down_task<RFPX_FP4>(a, tk, ed, slice, sm);
@@ -984,7 +988,10 @@ size_t prefill_layout(const moe_layer *L, int T, int xtype, void *args_out) {
   a.max_tasks = (L->n_experts + 1) + (a.rows_max + kChunk - 1) / kChunk;
   int nf = 0;
   for (int f = 0; f < 5; ++f) a.fmt_slot[f] = -1;
-  for (int e = 0; e <= L->n_experts; ++e) a.gu_fmts |= 1u << L->fmts[3 * e];
+  for (int e = 0; e <= L->n_experts; ++e) {
+    a.gu_fmts |= 1u << L->fmts[3 * e];
+    a.dn_fmts |= 1u << L->fmts[3 * e + 2];
+  }
   for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
     if ((a.gu_fmts >> f) & 1u) a.fmt_slot[f] = nf++;
   if (L->d % kTileDN || L->f % kTileGU) return 0;

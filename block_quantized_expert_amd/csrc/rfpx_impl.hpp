@@ -338,6 +338,15 @@ __device__ __forceinline__ uint32_t one_one_vgpr() {
   return r;
 }
 
+// The same constant from an asm statement without side effects: it orders
+// no memory access, so wave-uniform loads after it can still be scalar
+// loads (an asm volatile counts as a possible store for that analysis).
+__device__ __forceinline__ uint32_t one_one_vgpr_pure() {
+  uint32_t r;
+  asm("v_mov_b32 %0, 0x3f803f80" : "=v"(r));
+  return r;
+}
+
 // Decode the codes of one block into its 16 bf16 pair words (see the header
 // comment for the pairings).  `w` holds the block's code dwords: 2 (FP2),
 // 3 (FP3) or 4 (FP4); `one` is one_one_vgpr().
@@ -545,6 +554,10 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g));
 // ------------------------------------------------------------- host side
 // Internal host helpers (abi.hip, codec.hip).
 size_t image_layout(int d, int f, int E, const int *fmts, ExpertDesc *desc);
+// Host checks of a layer (abi.hip): shapes, limits and the format table;
+// the image pointer, its alignment and L->image_bytes against the layout.
+rfpx_status check_layer(const moe_layer *L);
+rfpx_status check_image(const moe_layer *L);
 void set_error(const char *fmt, ...);
 rfpx_status fail(rfpx_status st, const char *fmt, ...);
 

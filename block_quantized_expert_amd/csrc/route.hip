@@ -206,7 +206,8 @@ hipError_t launch_route(const ForwardPlan &p) {
   if (e != hipSuccess || !topk) return e;
   TopkArgs t{};
   t.rp = route_params(p);
-  t.image = p.image;
+  // moe_route_topk reads the router only: its image is never dereferenced
+  t.image = p.route_only ? nullptr : p.image;
   t.rt = reinterpret_cast<RouteTable *>(p.ws + p.wl.route);
   t.ids_out = p.ids_out;
   t.w_out = p.w_out;

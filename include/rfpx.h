@@ -51,9 +51,12 @@
  * Decode (q columns, [P3] "解码"): each packed block an expert needs is read
  * and decoded once per call and applied to every column that selected that
  * expert ([P2]: in the q=4 verify path each packed weight is decoded once
- * for all 4 columns).  Arithmetic is fp32 with exact weights and exact
- * activations; results differ from an exact evaluation only by fp32
- * summation order.
+ * for all 4 columns).  Dequantized weights are exact.  bf16 activations
+ * enter the products as they are; fp32 activations, and the hidden vector h
+ * of every expert, enter as a bf16 hi + bf16 lo pair (relative residual
+ * below 2^-16).  Every product is exact and sums are fp32, so results
+ * differ from an exact evaluation by fp32 summation order and that
+ * residual.
  *
  * ------------------------------------------------------------ conventions
  * - Every pointer named *_dev, and every pointer inside moe_layer except
@@ -112,9 +115,30 @@ size_t rfpx_matrix_bytes(int fmt, int rows, int cols);
  * Requires cols % 32 == 0, rows >= 0. */
 rfpx_status rfpx_pack(int fmt, const float *w_dev, int rows, int cols,
                       uint8_t *out_dev, size_t cap, void *stream);
+/* Importance-weighted quantizer ([P3] "ROCmFPX": weights are quantized with
+ * an importance matrix).  imp_dev[cols] >= 0 (finite) is the importance of
+ * each input column; block b of every row uses imp_dev[32b .. 32b+31].  Per
+ * block, with a = max|w|, the stored scale is the candidate of least
+ *     E(s) = sum_j imp_j * (w_j - (c_j - offset) * s)^2,
+ * codes c_j = nearest-even of w_j/s + offset, clamped, from the stored s.
+ * Candidates, tried in this order (a tie keeps the earlier one):
+ *   FP2/FP3: s = fp16 nearest-even of a / (offset * t), 65504 on overflow,
+ *            t = 1, 1+1/16, 1-1/16, 1+2/16, 1-2/16, ..., 1+8/16, 1-8/16
+ *            (t = 1 is rfpx_pack's absmax scale); s = 0 and repeats skipped;
+ *   FP4:     E8M0 e = e0, e0-1, e0+1 clamped to [1, 254], repeats skipped,
+ *            e0 = rfpx_pack's exponent.
+ * E is evaluated in double, term by term in column order, each operation
+ * rounded on its own.  a = 0 (or no candidate) gives all-zero bytes.  With
+ * every importance 0 the result equals rfpx_pack's. */
+rfpx_status rfpx_pack_weighted(int fmt, const float *w_dev, const float *imp_dev,
+                               int rows, int cols, uint8_t *out_dev, size_t cap,
+                               void *stream);
 /* Bit-pack codes_dev[rows][cols] (one code per byte, only the low 2/3/4
  * bits are used) and scale_bits_dev[rows][cols/32] (fp16 bit patterns for
- * FP2/FP3, E8M0 in the low byte for FP4) into canonical blocks. */
+ * FP2/FP3, E8M0 in the low byte for FP4) into canonical blocks.  Scale bits
+ * are device data and are packed as given: a non-finite scale (fp16 Inf or
+ * NaN, E8M0 = 255) is not rejected here; moe_image_validate reports every
+ * such block of an image built from these blocks. */
 rfpx_status rfpx_pack_codes(int fmt, const uint8_t *codes_dev,
                             const uint16_t *scale_bits_dev, int rows, int cols,
                             uint8_t *out_dev, size_t cap, void *stream);
@@ -153,7 +177,36 @@ typedef struct {
   const float *router_w;  /* device, [E][d] fp32 */
   const uint8_t *image;   /* device, built by moe_image_build for fmts */
   const int *fmts;        /* host, [(E+1)*3], the table the image was built with */
+  size_t image_bytes;     /* bytes of the image buffer: must equal
+                             moe_image_bytes(d, f, n_experts, fmts) */
 } moe_layer;
+
+/* Checks made on the host by every call that takes a moe_layer (before
+ * any launch): shapes and limits, the format table (known formats, gate
+ * and up of an expert alike), 256-byte alignment of the image and
+ * image_bytes == moe_image_bytes(d, f, n_experts, fmts) (RFPX_E_FORMAT
+ * otherwise).  The contents of the image are not read on the host; they
+ * are checked on the device by moe_image_validate, once per image.  Layer
+ * kernels skip, and leave no output for, any expert whose device table
+ * entry names a format absent from fmts. */
+
+/* Check an image on the device against L: its header, its expert table and
+ * every block scale ([P3] "ROCmFPX": FP2/FP3 blocks carry an fp16 scale, FP4
+ * blocks an E8M0 power of two).  Writes report_dev[4] (uint32, device,
+ * 4-byte aligned; overwritten, no initialization needed):
+ *   [0] header faults, a bit set: 1 magic, 2 version, 4 d, f or E differ
+ *       from L, 8 the recorded byte count differs from L->image_bytes;
+ *   [1] expert-table entries (expert, matrix) whose format or plane offsets
+ *       differ from the layout of L->fmts;
+ *   [2] blocks whose scale is not a finite number: an fp16 Inf or NaN
+ *       (FP2, FP3), or E8M0 = 255 (FP4; NaN in the OCP MX encoding);
+ *   [3] 0.
+ * All four zero: the layer kernels can use the image.  Two kernels on
+ * `stream` (the scan reads every scales plane: about 2.5% of the image);
+ * the report is valid once the stream has passed them.  Scales are read at
+ * the offsets that L->fmts implies, never at offsets read from the image,
+ * so a damaged table cannot send the scan outside the buffer. */
+rfpx_status moe_image_validate(const moe_layer *L, uint32_t *report_dev, void *stream);
 
 /* Dequantize matrix m of expert e straight from the image into w_dev
  * (rows x cols fp32) -- a check of the image layout. */
@@ -168,7 +221,8 @@ size_t moe_workspace_bytes(const moe_layer *L, int q_or_T, int prefill);
 
 /* Router scores, top-k and gating for q columns of x_dev ([q][d] fp32 or
  * bf16 per xtype): ids_dev[q][k] int32 (score descending, ties to the lower
- * index) and w_dev[q][k] fp32. */
+ * index) and w_dev[q][k] fp32.  Reads only router_w: L->image and
+ * L->image_bytes are neither read nor checked (either may be 0). */
 rfpx_status moe_route_topk(const moe_layer *L, const void *x_dev, int xtype,
                            int q, int32_t *ids_dev, float *w_dev, void *ws_dev,
                            size_t ws_bytes, void *stream);
@@ -217,6 +271,38 @@ rfpx_status moe_prefill_forward_timed(const moe_layer *L, const void *x_dev,
                                       int xtype, int T, float *y_dev,
                                       void *ws_dev, size_t ws_bytes,
                                       void *stream, void *const *events);
+
+/* ------------------------------------------------- dense projections
+ * [P2] "Lucebox 的优化三板斧": in the q-column verify step each packed dense
+ * weight is decoded once and applied to all columns; [P3] "ROCmFPX": dense
+ * and sensitive projections stay ROCmFP4 or wider.  A dense matrix W of
+ * rows x cols (rows a multiple of 64, cols a multiple of 32 -- of 64 for
+ * FP2 -- and at most 65536) lives in a dense image, a permutation of its
+ * canonical blocks: tiles of 64 rows; within a tile, chunk k (one block,
+ * two for FP2) of the 64 rows stored contiguously, row r of the tile at
+ * position r:
+ *   codes plane  [rows/64][chunks][64][16 | 12 | 16 bytes]
+ *   scales plane [rows/64][chunks][64][4 | 2 | 1 bytes], 256-byte aligned.
+ * Bytes of that image; 0 for an unsupported shape or format. */
+size_t rfpx_dense_image_bytes(int fmt, int rows, int cols);
+/* Build the dense image from canonical blocks canonical_dev (rows x cols/32
+ * blocks, row-major); image_dev 256-byte aligned, cap >= the image bytes. */
+rfpx_status rfpx_dense_image_build(int fmt, const uint8_t *canonical_dev, int rows,
+                                   int cols, uint8_t *image_dev, size_t cap, void *stream);
+/* Dequantize W from its dense image into w_dev[rows][cols] fp32 (exact). */
+rfpx_status rfpx_dense_image_unpack(int fmt, const uint8_t *image_dev, int rows, int cols,
+                                    float *w_dev, void *stream);
+/* Workspace of rfpx_dense_forward with q columns (any xtype); 0 if
+ * unsupported.  256-byte aligned, no initialization needed. */
+size_t rfpx_dense_workspace_bytes(int fmt, int rows, int cols, int q);
+/* y_dev[c][r] = sum_j W[r][j] x_dev[c][j] for c < q (1..RFPX_Q_MAX): x_dev
+ * [q][cols] bf16 or fp32 (16-byte aligned; fp32 enters as a bf16 hi + lo
+ * pair), y_dev [q][rows] fp32.  Every block is read and decoded once and
+ * applied to all q columns; products are exact, sums fp32 in a fixed
+ * order (y is the same bit for bit from run to run). */
+rfpx_status rfpx_dense_forward(int fmt, const uint8_t *image_dev, int rows, int cols,
+                               const void *x_dev, int xtype, int q, float *y_dev,
+                               void *ws_dev, size_t ws_bytes, void *stream);
 
 const char *rfpx_status_str(int status);
 const char *rfpx_last_error(void);

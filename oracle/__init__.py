@@ -61,6 +61,8 @@ def _load():
             "orc_gating": (None, [P, P, i, d, P]),
             "orc_expert_forward": (None, [P, i, P, i, P, i, i, i, P, P]),
             "orc_layer_forward": (None, [i, i, i, i, d, P, P, P, P, i, i, P, P, P]),
+            "orc_pack_weighted": (None, [i, P, P, i, i, P]),
+            "orc_dense_forward": (None, [i, P, i, i, P, i, i, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -120,6 +122,31 @@ def pack(fmt: int, w: np.ndarray) -> np.ndarray:
     out = np.empty(rows * (cols // 32) * block_bytes(fmt), np.uint8)
     _load().orc_pack(fmt, _p(w), rows, cols, _p(out))
     return out
+
+
+def pack_weighted(fmt: int, w: np.ndarray, imp: np.ndarray) -> np.ndarray:
+    """Importance-weighted quantizer: imp[cols] >= 0 per input column."""
+    w = np.ascontiguousarray(w, np.float32)
+    rows, cols = w.shape
+    imp = np.ascontiguousarray(imp, np.float32)
+    assert imp.shape == (cols,)
+    out = np.empty(rows * (cols // 32) * block_bytes(fmt), np.uint8)
+    _load().orc_pack_weighted(fmt, _p(w), _p(imp), rows, cols, _p(out))
+    return out
+
+
+def dense_forward(fmt: int, data: np.ndarray, rows: int, cols: int, x: np.ndarray,
+                  xtype: str) -> np.ndarray:
+    """y[q][rows] fp32 = W x_c for each column of x ([q][cols] fp32, or
+    uint16 bf16 bits with xtype "bf16")."""
+    data = np.ascontiguousarray(data, np.uint8)
+    assert data.size == rows * (cols // 32) * block_bytes(fmt)
+    xt = 1 if xtype == "bf16" else 0
+    x = np.ascontiguousarray(x, np.uint16 if xt else np.float32).reshape(-1, cols)
+    q = x.shape[0]
+    y = np.empty((q, rows), np.float32)
+    _load().orc_dense_forward(fmt, _p(data), rows, cols, _p(x), xt, q, _p(y))
+    return y
 
 
 def pack_codes(fmt: int, codes: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:

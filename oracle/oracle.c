@@ -214,6 +214,109 @@ void orc_pack(int fmt, const float *w, int rows, int cols, uint8_t *out) {
                      out + ((size_t)r * nb + b) * bb);
 }
 
+/* Importance-weighted quantizer ([P3] "ROCmFPX": the weights are quantized
+ * with an importance matrix).  The pages do not give the search; the one
+ * here is the plainest that uses a per-column importance:
+ *   error(block, s) = sum_j imp_j * (w_j - (c_j - o) * s)^2,
+ * codes c_j nearest (ties to even) to w_j / s + o, clamped, from the scale
+ * s as stored; the stored scale is the candidate of least error, the first
+ * one listed winning a tie.  Candidates, for a = max_j |w_j|:
+ *   FP2/FP3: s = fp16(a / (o * t)) for t = 1, 1 + 1/16, 1 - 1/16, 1 + 2/16,
+ *            1 - 2/16, ..., 1 + 8/16, 1 - 8/16 (t = 1 is the absmax scale);
+ *            a scale that overflows fp16 clamps to 65504, a scale of 0 or one
+ *            already listed is skipped;
+ *   FP4:     e = e0, e0 - 1, e0 + 1 with e0 the absmax exponent of
+ *            quantize_block, each clamped to [1, 254], repeats skipped.
+ * For a fixed scale the nearest code minimizes each weight's term on its
+ * own (the terms are independent and imp_j >= 0), so only the scale is
+ * searched.  a = 0 (or no candidate left) gives the all-zero block. */
+static double block_error(int fmt, const float *w, const float *imp,
+                          const int c[32], double s) {
+  double o = code_offset(fmt), err = 0.0;
+  for (int j = 0; j < 32; ++j) {
+    double d = (double)w[j] - ((double)c[j] - o) * s;
+    err += (double)imp[j] * (d * d);
+  }
+  return err;
+}
+
+static void codes_for_scale(int fmt, const float *w, double s, int c[32]) {
+  double o = code_offset(fmt);
+  double cmax = (double)((1 << code_bits(fmt)) - 1);
+  for (int j = 0; j < 32; ++j)
+    c[j] = (int)clampd(nearbyint((double)w[j] / s + o), 0.0, cmax);
+}
+
+static void quantize_block_weighted(int fmt, const float *w, const float *imp,
+                                    uint8_t *blk) {
+  int bb = orc_block_bytes(fmt);
+  double o = code_offset(fmt);
+  double a = 0.0;
+  for (int j = 0; j < 32; ++j)
+    if (fabs((double)w[j]) > a) a = fabs((double)w[j]);
+  memset(blk, 0, (size_t)bb);
+  if (a == 0.0) return;
+  int c[32], best_c[32];
+  double best = INFINITY;
+  int have = 0;
+  uint16_t best_bits = 0, seen[17];
+  int nseen = 0;
+  if (fmt == ORC_FP4) {
+    int ex;
+    double m = frexp(a / o, &ex);
+    int e0 = 127 + ((m == 0.5) ? ex - 1 : ex);
+    int cand[3] = {e0, e0 - 1, e0 + 1};
+    for (int i = 0; i < 3; ++i) {
+      int e = cand[i] < 1 ? 1 : (cand[i] > 254 ? 254 : cand[i]);
+      int dup = 0;
+      for (int k = 0; k < nseen; ++k) dup |= seen[k] == (uint16_t)e;
+      if (dup) continue;
+      seen[nseen++] = (uint16_t)e;
+      double s = ldexp(1.0, e - 127);
+      codes_for_scale(fmt, w, s, c);
+      double err = block_error(fmt, w, imp, c, s);
+      if (!have || err < best) {
+        have = 1;
+        best = err;
+        best_bits = (uint16_t)e;
+        memcpy(best_c, c, sizeof c);
+      }
+    }
+  } else {
+    for (int i = 0; i < 17; ++i) {
+      int k = (i + 1) / 2 * ((i & 1) ? 1 : -1); /* 0, 1, -1, 2, -2, ... */
+      double t = 1.0 + (double)k / 16.0;
+      uint16_t s16 = orc_double_to_half_rne(a / (o * t));
+      if ((s16 & 0x7FFF) == 0x7C00) s16 = 0x7BFF;
+      double s = orc_half_to_double(s16);
+      if (s == 0.0) continue;
+      int dup = 0;
+      for (int n = 0; n < nseen; ++n) dup |= seen[n] == s16;
+      if (dup) continue;
+      seen[nseen++] = s16;
+      codes_for_scale(fmt, w, s, c);
+      double err = block_error(fmt, w, imp, c, s);
+      if (!have || err < best) {
+        have = 1;
+        best = err;
+        best_bits = s16;
+        memcpy(best_c, c, sizeof c);
+      }
+    }
+  }
+  if (have) pack_one(fmt, best_c, best_bits, blk);
+}
+
+void orc_pack_weighted(int fmt, const float *w, const float *imp, int rows,
+                       int cols, uint8_t *out) {
+  int bb = orc_block_bytes(fmt);
+  int nb = cols / 32;
+  for (int r = 0; r < rows; ++r)
+    for (int b = 0; b < nb; ++b)
+      quantize_block_weighted(fmt, w + (size_t)r * cols + 32 * b, imp + 32 * b,
+                              out + ((size_t)r * nb + b) * bb);
+}
+
 /* ------------------------------------------------------------------ router */
 
 void orc_router_scores(const double *x, int q, int d, const float *wr, int E,
@@ -289,6 +392,26 @@ void orc_expert_forward(const uint8_t *gate, int fmt_gate, const uint8_t *up,
   qmatvec(fmt_down, down, d, f, g, o);
   free(g);
   free(u);
+}
+
+void orc_dense_forward(int fmt, const uint8_t *w, int rows, int cols,
+                       const void *x, int xtype, int q, float *y) {
+  /* [P2] "Lucebox 的优化三板斧": in the q-column verify step each packed
+   * dense weight is decoded once and applied to every column; the result is
+   * q independent products y_c = W x_c, which is what is computed here
+   * (decoding again for every column). */
+  double *xc = (double *)malloc(sizeof(double) * (size_t)cols);
+  double *yc = (double *)malloc(sizeof(double) * (size_t)rows);
+  for (int c = 0; c < q; ++c) {
+    if (xtype == 1)
+      orc_load_x((const uint16_t *)x + (size_t)c * cols, 1, cols, xc);
+    else
+      orc_load_x((const float *)x + (size_t)c * cols, 0, cols, xc);
+    qmatvec(fmt, w, rows, cols, xc, yc);
+    for (int r = 0; r < rows; ++r) y[(size_t)c * rows + r] = (float)yc[r];
+  }
+  free(xc);
+  free(yc);
 }
 
 void orc_load_x(const void *x, int xtype, int n, double *out) {

@@ -69,6 +69,20 @@ void orc_pack_codes(int fmt, const uint8_t *codes, const uint16_t *scale_bits,
  * block, codes rounded to nearest even from the rounded scale. */
 void orc_pack(int fmt, const float *w, int rows, int cols, uint8_t *out);
 
+/* Importance-weighted quantizer: per block the scale, among a fixed list
+ * of candidates around the absmax scale, that minimizes
+ * sum_j imp[col_j] * (w_j - dequantized w_j)^2 (oracle.c states the list
+ * and the tie rule); codes nearest from the stored scale.  imp[cols] >= 0
+ * is the importance of each input column. */
+void orc_pack_weighted(int fmt, const float *w, const float *imp, int rows,
+                       int cols, uint8_t *out);
+
+/* Dense q-column product y[c][r] = sum_j W[r][j] x[c][j] for a row-major
+ * block-quantized matrix W (rows x cols canonical blocks) and q columns of
+ * x (fp32, xtype 0, or bf16 bits, xtype 1); y[q][rows] fp32. */
+void orc_dense_forward(int fmt, const uint8_t *w, int rows, int cols,
+                       const void *x, int xtype, int q, float *y);
+
 /* Router scores s[c][e] = sum_i wr[e][i] * x[c][i]. */
 void orc_router_scores(const double *x, int q, int d, const float *wr, int E,
                        double *s);

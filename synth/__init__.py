@@ -86,6 +86,14 @@ WORKLOADS = {
 }
 
 
+# Layer instances a timed run rotates over (so that no weight is re-read
+# from the 256 MB last-level cache within a rotation; each layer image is
+# about 2.3 GB), and activation batches drawn per instance (variant 0..3).
+# The benchmark times these instances and the parity tests check every one.
+ROTATION = {DECODE_Q1: 8, VERIFY_Q4: 8, VERIFY_Q5: 43, PREFILL: 2}
+ACTIVATION_BATCHES = 4
+
+
 def _rng(*key: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
 

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     declared = header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 23
     assert set(declared) == set(bqe.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
@@ -79,23 +79,32 @@ def test_image_bytes_rejects_bad_tables(lib):
 
 
 class _Dummy:
-    """Stand-ins for device tensors: only data_ptr() is read, and every
-    call below fails validation before anything dereferences it."""
+    """Stand-ins for device tensors: only data_ptr() and numel() are read,
+    and every call below fails validation before anything dereferences
+    it."""
 
-    def __init__(self, ptr):
+    def __init__(self, ptr, n=0):
         self._p = ptr
+        self._n = n
         self.is_cuda = True
 
     def data_ptr(self):
         return self._p
 
+    def numel(self):
+        return self._n
+
     def is_contiguous(self):
         return True
 
 
-def _layer(d=256, f=128, E=8, k=2, fmts=None, image=4096, wr=8192):
+def _layer(d=256, f=128, E=8, k=2, fmts=None, image=4096, wr=8192, image_bytes=None):
+    """A layer whose image_bytes is, unless given, the layout of its table
+    (0 where the table itself is invalid)."""
     fm = _fmts(E) if fmts is None else fmts
-    return bqe.MoeLayer(d, f, E, k, _Dummy(wr), _Dummy(image), fm)
+    if image_bytes is None:
+        image_bytes = bqe.moe_image_bytes(d, f, E, fm) if E >= 1 else 0
+    return bqe.MoeLayer(d, f, E, k, _Dummy(wr), _Dummy(image, image_bytes), fm)
 
 
 def _fwd(lib, L, x=0x10000, xtype=0, q=1, y=0x20000, ws=0x30000, nbytes=1 << 30):
@@ -134,6 +143,40 @@ def test_forward_rejects_arguments(lib):
     fm = _fmts(8)
     fm[5, 2] = 9
     assert _fwd(lib, _layer(fmts=fm)) == -4
+
+
+def test_forward_checks_image_bytes(lib):
+    """image_bytes must equal the layout of the format table: one byte more
+    or less, or the layout of another table, is a format error."""
+    n = bqe.moe_image_bytes(256, 128, 8, _fmts(8))
+    for bad in (n - 1, n + 1, 0, bqe.moe_image_bytes(256, 128, 8, _fmts(8, hot=[1]))):
+        assert _fwd(lib, _layer(image_bytes=bad)) == -4
+        assert b"image_bytes" in lib.rfpx_last_error()
+        assert _pf(lib, _layer(image_bytes=bad)) == -4
+    assert _fwd(lib, _layer(image=0)) == -1
+
+
+def test_route_topk_does_not_check_the_image(lib):
+    """moe_route_topk reads only the router: a null image of size 0 passes
+    its host checks; the same layer is rejected by moe_layer_forward."""
+    L = _layer(image=0, image_bytes=0)
+    ids, w = C.c_void_p(0x40000), C.c_void_p(0x50000)
+    st = lib.moe_route_topk(L.ref, C.c_void_p(0x10000), 0, 1, ids, w,
+                            C.c_void_p(0x30010), 1 << 30, None)
+    assert st == -3  # it gets as far as the workspace alignment
+    assert _fwd(lib, L, ws=0x30010) == -1  # image is null
+
+
+def test_image_validate_host_checks(lib):
+    """moe_image_validate checks its arguments and image_bytes on the host."""
+    L = _layer()
+    rep = C.c_void_p(0x60000)
+    assert lib.moe_image_validate(L.ref, None, None) == -1
+    assert lib.moe_image_validate(L.ref, C.c_void_p(0x60002), None) == -3
+    assert lib.moe_image_validate(_layer(image_bytes=1).ref, rep, None) == -4
+    assert lib.moe_image_validate(_layer(image=4096 + 16).ref, rep, None) == -3
+    assert lib.moe_image_validate(_layer(d=300).ref, rep, None) == -2
+    assert lib.moe_image_unpack(_layer(image_bytes=5).ref, 0, 0, C.c_void_p(0x70000), None) == -4
 
 
 def _pf(lib, L, x=0x10000, xtype=1, T=64, y=0x20000, ws=0x30000, nbytes=1 << 32):
@@ -184,6 +227,34 @@ def test_codec_rejects_bad_arguments(lib):
     assert lib.rfpx_pack(2, p, 0, 64, p, 0, None) == 0  # empty matrix: nothing to do
     assert lib.rfpx_unpack(3, None, 4, 64, p, None) == -1
     assert lib.rfpx_pack_codes(4, p, None, 4, 64, p, 1 << 20, None) == -1
+    assert lib.rfpx_pack_weighted(2, p, None, 4, 64, p, 1 << 20, None) == -1
+    assert lib.rfpx_pack_weighted(7, p, p, 4, 64, p, 1 << 20, None) == -4
+    assert lib.rfpx_pack_weighted(3, p, p, 4, 40, p, 1 << 20, None) == -2
+    assert lib.rfpx_pack_weighted(4, p, p, 4, 64, p, 16, None) == -5
+
+
+def test_dense_host_checks(lib):
+    """Shapes, formats and arguments of the dense projection entry points,
+    all checked before any launch."""
+    assert lib.rfpx_dense_image_bytes(4, 64, 4096) == 64 * 128 * 16 + 64 * 128 * 1
+    assert lib.rfpx_dense_image_bytes(2, 128, 256) == 128 * 8 * 8 + 128 * 8 * 2
+    assert lib.rfpx_dense_image_bytes(3, 64, 96) == (64 * 3 * 12 + 255) // 256 * 256 + 64 * 3 * 2
+    assert lib.rfpx_dense_image_bytes(4, 100, 256) == 0     # rows not a multiple of 64
+    assert lib.rfpx_dense_image_bytes(2, 64, 96) == 0       # FP2 needs cols % 64
+    assert lib.rfpx_dense_image_bytes(5, 64, 256) == 0
+    assert lib.rfpx_dense_workspace_bytes(4, 4096, 4096, 9) == 0
+    assert lib.rfpx_dense_workspace_bytes(4, 4096, 4096, 5) > 0
+    p = C.c_void_p(0x1000)
+    fwd = lambda **k: lib.rfpx_dense_forward(  # noqa: E731
+        k.get("fmt", 4), k.get("img", p), k.get("rows", 64), k.get("cols", 256),
+        k.get("x", p), k.get("xt", 1), k.get("q", 1), k.get("y", p), k.get("ws", p),
+        k.get("nbytes", 1 << 30), None)
+    assert fwd(q=0) == -2 and fwd(q=9) == -2 and fwd(rows=65) == -2
+    assert fwd(fmt=7) == -4 and fwd(xt=2) == -1 and fwd(x=None) == -1
+    assert fwd(img=C.c_void_p(0x1010)) == -3 and fwd(x=C.c_void_p(0x1008)) == -3
+    assert fwd(nbytes=8) == -5
+    assert lib.rfpx_dense_image_build(4, p, 64, 256, p, 16, None) == -5
+    assert lib.rfpx_dense_image_build(4, None, 64, 256, p, 1 << 20, None) == -1
 
 
 def test_status_strings(lib):

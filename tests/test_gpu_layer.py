@@ -227,23 +227,6 @@ def test_verify_q4_zipf(bqe, decode_layer):
     assert_close(_run(bqe, L, cols.x), y_ref, what="q=4")
 
 
-# ------------------------------------- q=5 with the 32 hottest experts FP4
-
-@pytest.mark.parametrize("layer", [0, 21, 42])
-def test_verify_q5_hot_fp4(bqe, layer):
-    import torch
-    cfg = synth.WORKLOADS[synth.VERIFY_Q5]
-    lay = synth.gen_layer(cfg, layer)
-    L = bqe.upload_layer(lay)
-    cols = synth.gen_columns(cfg, lay, 5, layer=layer)
-    y = _run(bqe, L, cols.x)
-    with cf.ThreadPoolExecutor(5) as ex:
-        refs = list(ex.map(lambda c: _oracle(lay, cols.x[c:c + 1], "bf16")[0], range(5)))
-    assert_close(y, np.concatenate(refs), what=f"layer {layer}")
-    del L
-    torch.cuda.empty_cache()
-
-
 def test_decode_max_shape(bqe):
     """d = f = 4096 (the largest of both), k = 8 and q = 8 (the largest)
     together, bf16 and fp32 activations: every column against the oracle."""
@@ -260,4 +243,60 @@ def test_decode_max_shape(bqe):
             refs = list(ex.map(lambda c: _oracle(lay, cols.x[c:c + 1], xt)[0], range(8)))
         assert_close(y, np.concatenate(refs), what=f"{xt} q=8")
     del L
+    torch.cuda.empty_cache()
+
+
+def test_graph_of_layers_matches_oracle(bqe):
+    """Several layers of the q=5 verify workload captured as one HIP graph
+    (the multi-layer verify step run as one graph), replayed three times
+    with eager steps on other inputs in between: every replay gives each
+    layer's eager output bit for bit, and that output is within 2e-3 * RMS
+    of the oracle."""
+    import torch
+    cfg = synth.WORKLOADS[synth.VERIFY_Q5]
+    layers = (0, 17, 42)
+    Ls, xs, ys, wss, refs, xo = [], [], [], [], [], []
+    for l in layers:
+        lay = synth.gen_layer(cfg, l)
+        L = bqe.upload_layer(lay)
+        cols = synth.gen_columns(cfg, lay, 5, variant=1, layer=l)
+        other = synth.gen_columns(cfg, lay, 5, variant=2, layer=l)
+        with cf.ThreadPoolExecutor(5) as ex:
+            refs.append(np.concatenate(list(ex.map(
+                lambda c: _oracle(lay, cols.x[c:c + 1], "bf16")[0], range(5)))))
+        Ls.append(L)
+        xs.append(to_device_x(cols.x))
+        xo.append(to_device_x(other.x))
+        wss.append(bqe.workspace(L, 5))
+        ys.append(torch.empty((5, cfg.d), dtype=torch.float32, device="cuda"))
+        del lay
+
+    def step():
+        for L, x, y, ws in zip(Ls, xs, ys, wss):
+            bqe.moe_layer_forward(L, x, y=y, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    for y, ref, l in zip(eager, refs, layers):
+        assert_close(y.cpu().numpy(), ref, what=f"eager layer {l}")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        for L, x, ws in zip(Ls, xo, wss):
+            bqe.moe_layer_forward(L, x, ws=ws)  # eager, same workspaces
+        for y in ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e, l in zip(ys, eager, layers):
+            assert torch.equal(y, e), f"replay of layer {l}"
+    del g, Ls
     torch.cuda.empty_cache()

@@ -19,8 +19,9 @@ def bqe():
 
 
 def _router_layer(bqe, wr, k, f=128, fmts=None):
-    """Layer descriptor for routing only: the image is never read by
-    moe_route_topk, so a small aligned buffer stands in for it."""
+    """Layer descriptor for routing only: moe_route_topk reads the router
+    and nothing of the image (its header says so; the image pointer is not
+    passed to any of its kernels), so a small aligned buffer stands in."""
     import torch
     E, d = wr.shape
     fm = synth.expert_formats(E, np.arange(E), 0) if fmts is None else fmts

@@ -456,3 +456,133 @@ def test_bf16_activations_are_read_exactly():
     yb, _, _ = oracle.layer_forward_synth(lay, bits, "bf16")
     yf, _, _ = oracle.layer_forward_synth(lay, exact, "f32")
     assert np.array_equal(yb, yf)
+
+
+# ------------------------------------------- importance-weighted quantizer
+
+def _fp16_rne(v: float) -> float:
+    """numpy's double -> half conversion (round to nearest even), with the
+    quantizer's overflow clamp to 65504."""
+    h = float(np.float64(v).astype(np.float16))
+    return 65504.0 if math.isinf(h) else h
+
+
+def _weighted_candidates(fmt, a):
+    """The candidate scales of the importance-weighted quantizer, in order,
+    written out from its definition: t = 1, 1 + 1/16, 1 - 1/16, ..., for
+    FP2/FP3; e0, e0 - 1, e0 + 1 for FP4."""
+    out = []
+    if fmt == 4:
+        k = math.ceil(math.log2(a / 7.5))
+        if 7.5 * 2.0 ** (k - 1) >= a:
+            k -= 1
+        for e in (127 + k, 126 + k, 128 + k):
+            e = min(max(e, 1), 254)
+            if 2.0 ** (e - 127) not in out:
+                out.append(2.0 ** (e - 127))
+        return out
+    for i in range(17):
+        k = (i + 1) // 2 * (1 if i % 2 else -1)
+        s = _fp16_rne(a / (OFFSET[fmt] * (1 + k / 16)))
+        if s != 0.0 and s not in out:
+            out.append(s)
+    return out
+
+
+def _weighted_error(fmt, w, imp, codes, s):
+    err = 0.0
+    for j in range(32):
+        d = float(w[j]) - (codes[j] - OFFSET[fmt]) * s
+        err += float(imp[j]) * (d * d)
+    return err
+
+
+@pytest.mark.parametrize("fmt", [2, 3, 4])
+def test_weighted_pack_brute_force(fmt):
+    """Every block: the stored scale is the first candidate of least
+    importance-weighted error, the codes the exhaustive nearest codes of
+    that scale (errors summed in plain Python floats, in column order)."""
+    rng = np.random.default_rng(500 + fmt)
+    rows, cols = 6, 256
+    w = (rng.standard_normal((rows, cols)) * rng.choice([1e-3, 0.05, 2.0], (rows, 1))
+         ).astype(np.float32)
+    w[:, 5::37] *= 6.0                                     # outliers to clip or not
+    imp = rng.choice([0.0, 0.1, 1.0, 30.0], size=cols).astype(np.float32)
+    data = oracle.pack_weighted(fmt, w, imp)
+    bb = synth.BLOCK_BYTES[fmt]
+    raw = data.tobytes()
+    changed = 0
+    for r in range(rows):
+        for b in range(cols // 32):
+            blk = w[r, 32 * b:32 * b + 32].astype(np.float64)
+            im = imp[32 * b:32 * b + 32]
+            best = None
+            for s in _weighted_candidates(fmt, float(np.abs(blk).max())):
+                codes = _brute_codes(fmt, blk, s)
+                e = _weighted_error(fmt, blk, im, codes, s)
+                if best is None or e < best[0]:
+                    best = (e, s, codes)
+            i = r * (cols // 32) + b
+            codes, s = bigint_codes(fmt, raw[i * bb:(i + 1) * bb])
+            assert s == best[1] and codes == best[2], (r, b)
+            changed += s != _weighted_candidates(fmt, float(np.abs(blk).max()))[0]
+    assert changed > 0  # the search does move scales away from absmax
+
+
+@pytest.mark.parametrize("fmt", [2, 3, 4])
+def test_weighted_pack_not_worse_than_absmax(fmt):
+    """The absmax scale is a candidate, so no block's weighted error exceeds
+    the absmax quantizer's; with all importances 0 every error ties and the
+    first candidate, absmax, is kept: the bytes equal rfpx_pack's."""
+    rng = np.random.default_rng(600 + fmt)
+    w = (rng.standard_normal((16, 128)) * 0.05).astype(np.float32)
+    imp = (rng.standard_normal(128) ** 2).astype(np.float32)
+    wa = oracle.unpack(fmt, oracle.pack(fmt, w), 16, 128)
+    ww = oracle.unpack(fmt, oracle.pack_weighted(fmt, w, imp), 16, 128)
+    ea = ((wa - w) ** 2 * imp).reshape(16, 4, 32).sum(-1)
+    ew = ((ww - w) ** 2 * imp).reshape(16, 4, 32).sum(-1)
+    assert np.all(ew <= ea * (1 + 1e-12))
+    assert ew.sum() < ea.sum()
+    assert np.array_equal(oracle.pack_weighted(fmt, w, np.zeros(128, np.float32)),
+                          oracle.pack(fmt, w))
+
+
+def test_weighted_pack_invariances():
+    """Scaling every importance by a power of two leaves the choice alone;
+    a zero block stays all-zero bytes."""
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((8, 96)) * 0.1).astype(np.float32)
+    w[3, :32] = 0.0
+    imp = rng.random(96).astype(np.float32)
+    for fmt in (2, 3, 4):
+        a = oracle.pack_weighted(fmt, w, imp)
+        assert np.array_equal(a, oracle.pack_weighted(fmt, w, imp * 8.0))
+        bb = synth.BLOCK_BYTES[fmt]
+        assert not a[9 * bb:10 * bb].any()  # row 3, block 0
+
+
+# ------------------------------------------------------- dense projection
+
+@pytest.mark.parametrize("fmt,xtype", [(4, "bf16"), (2, "f32"), (3, "bf16")])
+def test_dense_forward_brute_force(fmt, xtype):
+    """y[c] = W x_c against numpy's product with the big-integer reader's
+    dense matrix, for q = 5 columns."""
+    rng = np.random.default_rng(700 + fmt)
+    rows, cols, q = 48, 160, 5
+    data = synth.random_matrix(800 + fmt, fmt, rows, cols, 0.05, 1e-3)
+    xf = rng.standard_normal((q, cols))
+    x = synth.to_bf16_bits(xf) if xtype == "bf16" else xf.astype(np.float32)
+    xd = synth.bf16_bits_to_f64(x) if xtype == "bf16" else x.astype(np.float64)
+    y = oracle.dense_forward(fmt, data, rows, cols, x, xtype)
+    want = xd @ dense(fmt, data, rows, cols).T
+    assert y.shape == (q, rows)
+    assert np.allclose(y, want, rtol=1e-6, atol=1e-6 * np.abs(want).max())
+
+
+def test_dense_forward_columns_are_independent():
+    rng = np.random.default_rng(9)
+    data = synth.random_matrix(901, 4, 64, 256)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    y = oracle.dense_forward(4, data, 64, 256, x, "f32")
+    for c in range(4):
+        assert np.array_equal(y[c:c + 1], oracle.dense_forward(4, data, 64, 256, x[c:c + 1], "f32"))
