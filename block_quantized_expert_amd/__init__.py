@@ -33,7 +33,8 @@ SYMBOLS = (
     "rfpx_unpack", "moe_image_bytes", "moe_image_build", "moe_image_validate",
     "moe_image_unpack",
     "moe_workspace_bytes", "moe_route_topk", "moe_layer_forward",
-    "moe_layer_forward_timed", "moe_prefill_forward", "moe_prefill_forward_timed",
+    "moe_layer_forward_timed", "moe_layer_forward_noalloc", "moe_noalloc_scratch_bytes",
+    "moe_prefill_forward", "moe_prefill_forward_timed",
     "rfpx_dense_image_bytes", "rfpx_dense_image_build", "rfpx_dense_image_unpack",
     "rfpx_dense_workspace_bytes", "rfpx_dense_forward",
     "rfpx_status_str", "rfpx_last_error",
@@ -94,6 +95,8 @@ def lib():
             "moe_route_topk": (I, [LP, P, I, I, P, P, P, S, P]),
             "moe_layer_forward": (I, [LP, P, I, I, P, P, S, P]),
             "moe_layer_forward_timed": (I, [LP, P, I, I, P, P, S, P, P]),
+            "moe_layer_forward_noalloc": (I, [LP, P, I, I, P, P]),
+            "moe_noalloc_scratch_bytes": (S, []),
             "moe_prefill_forward": (I, [LP, P, I, I, P, P, S, P]),
             "moe_prefill_forward_timed": (I, [LP, P, I, I, P, P, S, P, P]),
             "rfpx_dense_image_bytes": (S, [I, I, I]),
@@ -357,6 +360,15 @@ def moe_layer_forward_timed(layer: MoeLayer, x, y, ws, events, stream=None):
     _check("moe_layer_forward_timed", lib().moe_layer_forward_timed(
         layer.ref, _ptr(x), _xtype(x), x.shape[0], _ptr(y), _ptr(ws), ws.numel(),
         _stream(stream), C.cast(events, C.c_void_p) if events is not None else None))
+    return y
+
+
+def moe_layer_forward_noalloc(layer: MoeLayer, x, y, stream=None):
+    """moe_layer_forward on the library's own device scratch: y (cuda fp32
+    [q][d]) is given by the caller, nothing is allocated."""
+    _need_cuda(x, y)
+    _check("moe_layer_forward_noalloc", lib().moe_layer_forward_noalloc(
+        layer.ref, _ptr(x), _xtype(x), x.shape[0], _ptr(y), _stream(stream)))
     return y
 
 

@@ -10,11 +10,45 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "rfpx_impl.hpp"
 
 namespace rfpx {
 
+// Device scratch of moe_layer_forward_noalloc: the decode workspace of one
+// call, for callers that cannot allocate.  Every GPU the library runs on
+// holds its own copy (loaded with the code object, kept until the process
+// ends).  In host code `scratch` names a host-side stand-in; the device
+// address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with the device current).
+static rfpx_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RFPX_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RFPX_E_ARG, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(RFPX_E_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RFPX_OK;
+}
 
 static thread_local char g_err[512];
 
@@ -295,6 +329,25 @@ rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x, int xtype
   hipError_t e = launch_route(p);
   if (e == hipSuccess) e = launch_experts(p);
   return e == hipSuccess ? RFPX_OK : fail(RFPX_E_HIP, "moe_layer_forward: %s", hipGetErrorString(e));
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+rfpx_status moe_layer_forward_noalloc(const moe_layer *L, const void *x, int xtype, int q,
+                                      float *y, void *stream) {
+  ForwardPlan p;
+  rfpx_status st = make_plan(L, q, xtype, &p);
+  if (st) return st;
+  if ((st = check_inputs(L, x, true))) return st;
+  if (!y) return fail(RFPX_E_ARG, "y is null");
+  if (p.wl.total > kScratchBytes)
+    return fail(RFPX_E_WORKSPACE,
+                "moe_layer_forward_noalloc: this shape needs %zu bytes of workspace, the "
+                "library's scratch holds %zu; use moe_layer_forward with a workspace",
+                p.wl.total, kScratchBytes);
+  void *ws = nullptr;
+  if ((st = scratch_address(&ws))) return st;
+  return moe_layer_forward(L, x, xtype, q, y, ws, kScratchBytes, stream);
 }
 
 rfpx_status moe_prefill_forward(const moe_layer *L, const void *x, int xtype, int T,

@@ -249,6 +249,24 @@ rfpx_status moe_layer_forward_timed(const moe_layer *L, const void *x_dev,
                                     void *ws_dev, size_t ws_bytes,
                                     void *stream, void *const *events);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is the library's own device scratch of
+ * moe_noalloc_scratch_bytes() bytes (8 MiB), one per GPU, held until the
+ * process ends.  Nothing is allocated or freed; the caller passes x_dev and
+ * y_dev as for moe_layer_forward.  A shape whose workspace
+ * (moe_workspace_bytes for the given xtype) exceeds the scratch is rejected
+ * with RFPX_E_WORKSPACE before any launch; the spec shapes (d = 4096,
+ * f = 2048, E = 256, k = 6, q <= 8) fit, the largest shapes (d = f = 4096,
+ * k = q = 8) do not.  The scratch needs no initialization (the step writes
+ * everything it reads).  All calls on one GPU share its scratch: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must
+ * be serialized by the caller. */
+rfpx_status moe_layer_forward_noalloc(const moe_layer *L, const void *x_dev, int xtype,
+                                      int q, float *y_dev, void *stream);
+/* Bytes of the scratch moe_layer_forward_noalloc uses (8 MiB). */
+size_t moe_noalloc_scratch_bytes(void);
+
 /* One prefill chunk of T tokens (x_dev [T][d] bf16 or fp32): tokens are
  * grouped by expert and each expert runs as a dense grouped product on the
  * matrix cores.  y_dev[T][d] fp32.  ([P3] "稀疏预填充": prefill is batched per

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     declared = header_functions()
-    assert len(declared) == 23
+    assert len(declared) == 25
     assert set(declared) == set(bqe.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
@@ -165,6 +165,24 @@ def test_route_topk_does_not_check_the_image(lib):
                             C.c_void_p(0x30010), 1 << 30, None)
     assert st == -3  # it gets as far as the workspace alignment
     assert _fwd(lib, L, ws=0x30010) == -1  # image is null
+
+
+def test_noalloc_rejects_before_any_launch(lib):
+    """moe_layer_forward_noalloc makes the checks of moe_layer_forward, and
+    refuses a shape whose workspace exceeds the library's scratch, before
+    it touches the device."""
+    assert lib.moe_noalloc_scratch_bytes() == 8 << 20
+    L = _layer()
+    x, y = C.c_void_p(0x10000), C.c_void_p(0x20000)
+    assert lib.moe_layer_forward_noalloc(L.ref, x, 0, 9, y, None) == -2
+    assert lib.moe_layer_forward_noalloc(_layer(image_bytes=3).ref, x, 0, 1, y, None) == -4
+    big = _layer(d=4096, f=4096, E=64, k=8, fmts=_fmts(64))
+    assert bqe.moe_workspace_bytes(big, 8) > 8 << 20
+    assert lib.moe_layer_forward_noalloc(big.ref, x, 1, 8, y, None) == -5
+    assert b"scratch" in lib.rfpx_last_error()
+    # the north-star shapes fit (a q=8 step of the d=4096, E=256, k=6 layer)
+    ns = _layer(d=4096, f=2048, E=256, k=6, fmts=_fmts(256))
+    assert bqe.moe_workspace_bytes(ns, 8) <= 8 << 20
 
 
 def test_image_validate_host_checks(lib):
