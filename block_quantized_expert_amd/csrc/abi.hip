@@ -207,6 +207,20 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
     return fail(RFPX_E_SHAPE, "d=%d: no down tile for this format mix", L->d);
   // per-wave accumulators of the down tile in LDS: fewer waves when a wide
   // tile (short rows make long units) and many columns would not fit
+  if (q == 1) {
+    // one-column steps deal the units of the k + 1 slots round-robin: no
+    // more waves than the most units a tile can hold (7 at k = 6 with one
+    // unit per slot), kept a multiple of the column parts
+    int per_slot = 1, parts = 1;
+    for (int f = RFPX_FP2; f <= RFPX_FP4; ++f)
+      if ((p->down_fmts >> f) & 1u) {
+        const int u = p->rw_dn / (unit_rows_for(f, 1) * p->geo_dn[f].rpi) * p->geo_dn[f].tpl;
+        per_slot = per_slot > u ? per_slot : u;
+        parts = parts > p->geo_dn[f].tpl ? parts : p->geo_dn[f].tpl;
+      }
+    const int units = (L->top_k + 1) * per_slot;
+    if (units < p->wmax) p->wmax = (units + parts - 1) / parts * parts;
+  }
   while (p->wmax > 2 && (size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024) p->wmax /= 2;
   if ((size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024)
     return fail(RFPX_E_SHAPE, "f=%d, q=%d: down tile of %d rows needs too much LDS", L->f, q,

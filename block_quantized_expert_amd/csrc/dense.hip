@@ -19,32 +19,32 @@
 // (scalar loads, held in scalar registers), and each lane accumulates its
 // own row for every column, so no cross-lane reduction is needed.
 //
-// Launches: k_dense_prep (prepared activations: bf16 pair words in the
-// format's decode order plus each block's accumulator start, as for the
-// expert kernels), k_dense (grid tiles x splits; the waves of a workgroup
-// split the tile's chunks, their sums meet in LDS in a fixed order), and,
-// when a tile's chunks are split over several workgroups, k_dense_sum (the
-// splits' partial sums in split order).  y is the same bit for bit from run
-// to run.
+// Launches: k_dense (grid tiles x splits; the waves of a workgroup split
+// the tile's chunks, their sums meet in LDS in a fixed order) and, when a
+// tile's chunks are split over several workgroups (fewer than 256 tiles),
+// k_dense_sum (the splits' partial sums in split order).  A workgroup first
+// issues all its weight loads, then, while they are in flight, prepares the
+// activations of its blocks (bf16 pair words in the format's decode order
+// and each block's accumulator start, as for the expert kernels) into LDS,
+// where every lane of a wave reads the same words (broadcast reads).  y is
+// the same bit for bit from run to run.
 #include "rfpx_impl.hpp"
 
 namespace rfpx {
 namespace {
 
 constexpr int kDenseWavesMax = 8;
-constexpr int kDenseCpwMax = 8;  // chunks in flight per wave (8 KiB of FP4 codes)
+constexpr int kDenseCpwMax = 16;  // blocks in flight per wave (16 KiB of FP4 codes)
+constexpr size_t kDenseLdsMax = 64 * 1024;  // dynamic LDS of one workgroup
 
 struct DenseArgs {
   const uint8_t *codes;    // codes plane
   const uint8_t *scales;   // scales plane
   const void *x;
-  const uint32_t *xp;      // [q][nb][vx][16]
-  const float *xnc;        // [q][nb]
   float *y;                // [q][rows]
   float *part;             // [splits][q][rows] (splits > 1)
   int rows, cols, nb, nch, q, xtype, vx;
   int waves, cpw, splits;  // chunks per wave; workgroups per tile
-  int n_prep;              // q * nb prepared blocks
 };
 
 template <int FMT>
@@ -56,11 +56,10 @@ struct DFmt {
   static constexpr int SBYTES = CB * scale_bytes(FMT);
 };
 
-// Prepared activations of block b of column c.
+// Prepared activations of block b of column c into dst (vx * 16 words) and
+// its accumulator start into *nc.
 template <int FMT>
-__device__ void dense_prep_item(const DenseArgs &a, int c, int b) {
-  const size_t item = (size_t)c * a.nb + b;
-  uint32_t *dst = const_cast<uint32_t *>(a.xp) + item * (size_t)a.vx * 16;
+__device__ void dense_prep_item(const DenseArgs &a, int c, int b, uint32_t *dst, float *nc) {
   uint32_t hi[32], lo[32], pw[16];
   float nc_hi, nc_lo = 0.f;
   if (a.xtype == RFPX_X_BF16) {
@@ -93,20 +92,15 @@ __device__ void dense_prep_item(const DenseArgs &a, int c, int b) {
   }
   prep_pairs<FMT>(hi, pw, &nc_hi);
 #pragma unroll
-  for (int p = 0; p < 16; ++p) dst[p] = pw[p];
+  for (int p = 0; p < 16; p += 4)
+    *reinterpret_cast<uint4 *>(dst + p) = make_uint4(pw[p], pw[p + 1], pw[p + 2], pw[p + 3]);
   if (a.vx == 2) {
     prep_pairs<FMT>(lo, pw, &nc_lo);
 #pragma unroll
-    for (int p = 0; p < 16; ++p) dst[16 + p] = pw[p];
+    for (int p = 0; p < 16; p += 4)
+      *reinterpret_cast<uint4 *>(dst + 16 + p) = make_uint4(pw[p], pw[p + 1], pw[p + 2], pw[p + 3]);
   }
-  const_cast<float *>(a.xnc)[item] = nc_hi + nc_lo;
-}
-
-template <int FMT>
-__global__ __launch_bounds__(256) void k_dense_prep(DenseArgs a) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= a.n_prep) return;
-  dense_prep_item<FMT>(a, i / a.nb, i % a.nb);
+  *nc = nc_hi + nc_lo;
 }
 
 template <int FMT>
@@ -134,12 +128,14 @@ __device__ __forceinline__ void dense_load(__amdgpu_buffer_rsrc_t rc, __amdgpu_b
 
 // Tile blockIdx.x, split blockIdx.y: wave w takes chunks
 // (split * waves + w) * cpw .. + cpw of the tile's rows, all loads issued
-// before the arithmetic; each lane accumulates its row for the Q columns.
+// first; the workgroup's prepared activations go to LDS meanwhile; each lane
+// then accumulates its row for the Q columns.  LDS: the prepared words
+// [Q][blocks][VX * 16], their starts [Q][blocks], the wave sums [waves][Q][64].
 template <int FMT, int Q, int VX>
 __global__ __launch_bounds__(64 * kDenseWavesMax) void k_dense(DenseArgs a) {
   using F = DFmt<FMT>;
-  constexpr int CPW_MAX = kDenseCpwMax;
-  __shared__ float red[kDenseWavesMax][Q][64];
+  constexpr int CPW_MAX = kDenseCpwMax / F::CB;  // 16 blocks in flight per wave
+  extern __shared__ __align__(16) uint32_t lds[];
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
   const int tile = blockIdx.x, split = blockIdx.y;
   const int k0 = (split * a.waves + wave) * a.cpw;
@@ -148,49 +144,64 @@ __global__ __launch_bounds__(64 * kDenseWavesMax) void k_dense(DenseArgs a) {
       make_rsrc(a.codes + (tile_chunks + k0) * 64 * F::CBYTES, (uint32_t)(a.cpw * 64 * F::CBYTES));
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(a.scales + (tile_chunks + k0) * 64 * F::SBYTES, (uint32_t)(a.cpw * 64 * F::SBYTES));
+  // every load unconditional: chunks past cpw lie past the buffer
+  // resources' ranges and read as zero without a memory access (a guard
+  // per load would make the compiler wait for each load before the next)
   uint32_t cw[CPW_MAX][F::CW], sw[CPW_MAX];
 #pragma unroll
   for (int i = 0; i < CPW_MAX; ++i)
-    if (i < a.cpw)
-      dense_load<FMT>(rc, rs, (uint32_t)((i * 64 + lane) * F::CBYTES),
-                      (uint32_t)((i * 64 + lane) * F::SBYTES), cw[i], sw[i]);
+    dense_load<FMT>(rc, rs, (uint32_t)((i * 64 + lane) * F::CBYTES),
+                    (uint32_t)((i * 64 + lane) * F::SBYTES), cw[i], sw[i]);
+  // the workgroup's blocks b0 .. b0 + nbw of every column, prepared into LDS
+  const int nbw = a.waves * a.cpw * F::CB, b0 = split * nbw;
+  uint32_t *xw_lds = lds;                                            // [Q][nbw][VX*16]
+  float *nc_lds = reinterpret_cast<float *>(lds + (size_t)Q * nbw * VX * 16);  // [Q][nbw]
+  float *red = nc_lds + Q * nbw;                                      // [waves][Q][64]
+  for (int it = threadIdx.x; it < Q * nbw; it += blockDim.x) {
+    const int c = it / nbw, bl = it % nbw;
+    dense_prep_item<FMT>(a, c, b0 + bl, xw_lds + (size_t)it * VX * 16, nc_lds + it);
+  }
+  __syncthreads();
   float acc[Q];
 #pragma unroll
   for (int c = 0; c < Q; ++c) acc[c] = 0.f;
   const uint32_t one = one_one_vgpr_pure();
-  const uint32_t *__restrict__ xp = a.xp;
-  const float *__restrict__ xnc = a.xnc;
 #pragma unroll
   for (int i = 0; i < CPW_MAX; ++i) {
-    if (i >= a.cpw) break;
+    if (i < a.cpw) {
 #pragma unroll
     for (int j = 0; j < F::CB; ++j) {
-      const int b = (k0 + i) * F::CB + j;  // block column (wave-uniform)
+      const int bl = (wave * a.cpw + i) * F::CB + j;  // block within the workgroup
       uint32_t pr[16];
       decode_pairs<FMT>(&cw[i][j * F::BW], pr, one);
       const float s = block_scale<FMT>(FMT == RFPX_FP2 ? (sw[i] >> (16 * j)) : sw[i]);
 #pragma unroll
       for (int c = 0; c < Q; ++c) {
-        const uint32_t *xw = xp + ((size_t)c * a.nb + b) * VX * 16;
-        float t0 = xnc[(size_t)c * a.nb + b], t1 = 0.f;
+        // every lane reads the same words: broadcast LDS reads
+        const uint4 *xv = reinterpret_cast<const uint4 *>(xw_lds + ((size_t)c * nbw + bl) * VX * 16);
+        float t0 = nc_lds[c * nbw + bl], t1 = 0.f;
 #pragma unroll
         for (int v = 0; v < VX; ++v)
 #pragma unroll
-          for (int p = 0; p < 16; p += 2) {
-            t0 = dot2(xw[v * 16 + p], pr[p], t0);
-            t1 = dot2(xw[v * 16 + p + 1], pr[p + 1], t1);
+          for (int u = 0; u < 4; ++u) {
+            const uint4 w4 = xv[4 * v + u];
+            t0 = dot2(w4.x, pr[4 * u + 0], t0);
+            t1 = dot2(w4.y, pr[4 * u + 1], t1);
+            t0 = dot2(w4.z, pr[4 * u + 2], t0);
+            t1 = dot2(w4.w, pr[4 * u + 3], t1);
           }
         acc[c] = fmaf(t0 + t1, s, acc[c]);
       }
     }
+    }
   }
 #pragma unroll
-  for (int c = 0; c < Q; ++c) red[wave][c][lane] = acc[c];
+  for (int c = 0; c < Q; ++c) red[(wave * Q + c) * 64 + lane] = acc[c];
   __syncthreads();
   for (int i = threadIdx.x; i < Q * 64; i += blockDim.x) {
     const int c = i / 64, l = i % 64;
     float v = 0.f;
-    for (int w = 0; w < a.waves; ++w) v += red[w][c][l];
+    for (int w = 0; w < a.waves; ++w) v += red[(w * Q + c) * 64 + l];
     const size_t row = (size_t)tile * 64 + l;
     if (a.splits == 1) a.y[(size_t)c * a.rows + row] = v;
     else a.part[((size_t)split * Q + c) * a.rows + row] = v;
@@ -242,9 +253,13 @@ __global__ __launch_bounds__(256) void k_dense_image(int fmt, const uint8_t *__r
 
 struct DensePlan {
   int nb, nch, waves, cpw, splits, vx;
-  size_t codes_bytes, scales_off, image_bytes;
-  size_t ws_xp, ws_xnc, ws_part, ws_total;
+  size_t codes_bytes, scales_off, image_bytes, lds, ws_total;
 };
+
+// LDS of one k_dense workgroup: prepared words, starts and wave sums.
+size_t dense_lds(int q, int vx, int nbw, int waves) {
+  return (size_t)q * nbw * vx * 64 + (size_t)q * nbw * 4 + (size_t)waves * q * 64 * 4;
+}
 
 rfpx_status dense_plan(int fmt, int rows, int cols, int q, int xtype, DensePlan *p) {
   if (!valid_fmt(fmt)) return fail(RFPX_E_FORMAT, "unknown format %d", fmt);
@@ -253,7 +268,7 @@ rfpx_status dense_plan(int fmt, int rows, int cols, int q, int xtype, DensePlan 
                 "(at most 65536)", rows, cols);
   const int nb = cols / 32, CB = chunk_blocks(fmt);
   if (nb % CB) return fail(RFPX_E_SHAPE, "dense FP2 needs cols a multiple of 64");
-  if (q < 0 || q > kQMax) return fail(RFPX_E_SHAPE, "q=%d: must be in [1, %d]", q, kQMax);
+  if (q < 1 || q > kQMax) return fail(RFPX_E_SHAPE, "q=%d: must be in [1, %d]", q, kQMax);
   if (xtype != RFPX_X_F32 && xtype != RFPX_X_BF16) return fail(RFPX_E_ARG, "xtype=%d", xtype);
   p->nb = nb;
   p->nch = nb / CB;
@@ -265,25 +280,25 @@ rfpx_status dense_plan(int fmt, int rows, int cols, int q, int xtype, DensePlan 
   // waves per workgroup: at most 8 and a power of two dividing the chunks
   int waves = kDenseWavesMax;
   while (waves > 1 && p->nch % waves) waves /= 2;
-  const int per_tile = p->nch / waves;  // chunk runs per wave and split
+  const int per_tile = p->nch / waves;  // chunk runs per wave over all splits
   const int tiles = rows / 64;
-  // chunks per wave: the largest power of two up to kDenseCpwMax dividing
-  // the tile's chunks per wave; the rest of the tile goes to further
-  // workgroups (splits)
-  int cpw = kDenseCpwMax;
-  while (cpw > 1 && per_tile % cpw) cpw /= 2;
-  (void)tiles;
+  // chunks per wave: a power of two dividing per_tile, at most
+  // kDenseCpwMax, small enough that the launch has a workgroup per compute
+  // unit (256) and that the workgroup's prepared activations fit in LDS;
+  // the rest of a tile goes to further workgroups (splits)
+  long long want = (long long)per_tile * tiles / 256;
+  int cpw = kDenseCpwMax / CB;
+  while (cpw > 1 && (per_tile % cpw || cpw > want ||
+                     dense_lds(q, p->vx, waves * cpw * CB, waves) > kDenseLdsMax))
+    cpw /= 2;
   p->waves = waves;
   p->cpw = cpw;
   p->splits = per_tile / cpw;
-  size_t off = 0;
-  p->ws_xp = off;
-  off = align_up(off + (size_t)kQMax * nb * p->vx * 16 * 4, 256);
-  p->ws_xnc = off;
-  off = align_up(off + (size_t)kQMax * nb * 4, 256);
-  p->ws_part = off;
-  off = align_up(off + (p->splits > 1 ? (size_t)p->splits * (q ? q : kQMax) * rows * 4 : 0), 256);
-  p->ws_total = off;
+  p->lds = dense_lds(q, p->vx, waves * cpw * CB, waves);
+  if (p->lds > kDenseLdsMax)
+    return fail(RFPX_E_SHAPE, "dense %dx%d at q=%d: one chunk per wave needs %zu bytes of LDS",
+                rows, cols, q, p->lds);
+  p->ws_total = align_up(p->splits > 1 ? (size_t)p->splits * q * rows * 4 : 0, 256);
   return RFPX_OK;
 }
 
@@ -349,9 +364,13 @@ rfpx_status rfpx_dense_image_unpack(int fmt, const uint8_t *image, int rows, int
 }
 
 size_t rfpx_dense_workspace_bytes(int fmt, int rows, int cols, int q) {
-  DensePlan p;
-  if (q < 1 || dense_plan(fmt, rows, cols, q, RFPX_X_F32, &p)) return 0;
-  return p.ws_total;
+  DensePlan p16, p32;
+  if (dense_plan(fmt, rows, cols, q, RFPX_X_BF16, &p16) ||
+      dense_plan(fmt, rows, cols, q, RFPX_X_F32, &p32))
+    return 0;
+  // at least 256 bytes, so that a valid shape never reads as "unsupported"
+  const size_t n = p16.ws_total > p32.ws_total ? p16.ws_total : p32.ws_total;
+  return n > 256 ? n : 256;
 }
 
 rfpx_status rfpx_dense_forward(int fmt, const uint8_t *image, int rows, int cols, const void *x,
@@ -371,10 +390,7 @@ rfpx_status rfpx_dense_forward(int fmt, const uint8_t *image, int rows, int cols
   a.codes = image;
   a.scales = image + p.scales_off;
   a.x = x;
-  uint8_t *w8 = static_cast<uint8_t *>(ws);
-  a.xp = reinterpret_cast<const uint32_t *>(w8 + p.ws_xp);
-  a.xnc = reinterpret_cast<const float *>(w8 + p.ws_xnc);
-  a.part = reinterpret_cast<float *>(w8 + p.ws_part);
+  a.part = reinterpret_cast<float *>(ws);
   a.y = y;
   a.rows = rows;
   a.cols = cols;
@@ -386,20 +402,13 @@ rfpx_status rfpx_dense_forward(int fmt, const uint8_t *image, int rows, int cols
   a.waves = p.waves;
   a.cpw = p.cpw;
   a.splits = p.splits;
-  a.n_prep = q * p.nb;
   hipStream_t s = (hipStream_t)stream;
-  const dim3 gp((unsigned)((a.n_prep + 255) / 256));
-  hipError_t e;
-  if (fmt == RFPX_FP2) e = launch_k(k_dense_prep<RFPX_FP2>, gp, dim3(256), 0, s, a);
-  else if (fmt == RFPX_FP3) e = launch_k(k_dense_prep<RFPX_FP3>, gp, dim3(256), 0, s, a);
-  else e = launch_k(k_dense_prep<RFPX_FP4>, gp, dim3(256), 0, s, a);
-  if (e != hipSuccess) return fail(RFPX_E_HIP, "rfpx_dense_forward: %s", hipGetErrorString(e));
   const bool bf = p.vx == 1;
   void *k = fmt == RFPX_FP2 ? (bf ? dense_kernel<RFPX_FP2, 1>(q) : dense_kernel<RFPX_FP2, 2>(q))
           : fmt == RFPX_FP3 ? (bf ? dense_kernel<RFPX_FP3, 1>(q) : dense_kernel<RFPX_FP3, 2>(q))
                             : (bf ? dense_kernel<RFPX_FP4, 1>(q) : dense_kernel<RFPX_FP4, 2>(q));
   void *args[] = {&a};
-  e = hipLaunchKernel(k, dim3(rows / 64, p.splits), dim3(64 * p.waves), args, 0, s);
+  hipError_t e = hipLaunchKernel(k, dim3(rows / 64, p.splits), dim3(64 * p.waves), args, p.lds, s);
   if (e == hipSuccess && p.splits > 1) {
     const size_t n = (size_t)q * rows;
     e = launch_k(k_dense_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);

@@ -763,12 +763,20 @@ __device__ __forceinline__ void down_slot_run(const ExpArgs &a, const SlotCols &
 
 // The units of one slot that fall to this wave: units are dealt to the
 // waves round-robin in slot order (`item` counts the units dealt so far).
+// Only a wave that owns one of the slot's units builds the slot's buffer
+// resources.
 template <int FMT, int G>
 __device__ __forceinline__ void down_slot(const ExpArgs &a, const SlotCols &sc, int slot,
                                           const ExpertDesc &ed, int r0, int wave, int waves,
                                           int &item, float *accw) {
   constexpr int R = unit_rows_for(FMT, G);
   const Geo geo = a.geo_dn[FMT];
+  const int P = geo.tpl;
+  const int units = a.rw_dn / (R * geo.rpi) * P;
+  // this wave's first unit of the slot: (item + u) % waves == wave
+  const int first = (wave - item % waves + waves) % waves;
+  item += units;
+  if (first >= units) return;
   const uint32_t cpitch = (uint32_t)(a.f / 32) * code_bytes(FMT);
   const uint32_t spitch = (uint32_t)(a.f / 32) * scale_bytes(FMT);
   const MatPtr mats[1] = {
@@ -776,10 +784,7 @@ __device__ __forceinline__ void down_slot(const ExpArgs &a, const SlotCols &sc, 
   // FP2 chunks hold two blocks, so two-column passes would need 128
   // registers of h: FP2 down matrices take one column per pass
   constexpr int GD = FMT == RFPX_FP2 ? 1 : G;
-  const int P = geo.tpl;
-  const int units = a.rw_dn / (R * geo.rpi) * P;
-  for (int u = 0; u < units; ++u, ++item) {
-    if (item % waves != wave) continue;
+  for (int u = first; u < units; u += waves) {
     const UnitPos up = unit_pos(u, P, R, geo.rpi);
     for (int c0 = 0; c0 < sc.ncols; c0 += GD) {
       if constexpr (GD == 2) {
