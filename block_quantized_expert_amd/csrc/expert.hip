@@ -126,9 +126,14 @@ struct MatPtr {
 
 // Code and scale loads of one unit: rows row_u + rpi*i (i < R) of NM
 // matrices, the lane's own chunk at byte offsets coff (codes) and soff
-// (scales) within a row; rows are addressed through the planes' buffer
-// resources at scalar offset row * pitch (row_u is wave-uniform).
-template <int FMT, int NM, int R>
+// (scales) within a row, through the planes' buffer resources.  By default
+// a row's offset row * pitch is the scalar operand (no extra registers).
+// With LANE_ROW it joins the lane operand instead, which the buffer range
+// check covers: a row past the matrix (the "next unit" after a wave's last
+// one) then reads as zero with no memory access, so a prefetch of the next
+// unit needs no branch -- a branch around it makes the compiler wait for
+// the prefetch before computing the current unit.
+template <int FMT, int NM, int R, bool LANE_ROW = false>
 __device__ __forceinline__ void unit_load(const MatPtr (&mats)[NM], uint32_t cpitch,
                                           uint32_t spitch, int row_u, int rpi, uint32_t coff,
                                           uint32_t soff, uint32_t (&cw)[R][NM][Fmt<FMT>::CW],
@@ -138,8 +143,13 @@ __device__ __forceinline__ void unit_load(const MatPtr (&mats)[NM], uint32_t cpi
     const uint32_t row = (uint32_t)(row_u + rpi * i);
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      load_chunk<FMT>(mats[m].codes, coff, row * cpitch, cw[i][m]);
-      sw[i][m] = load_scale<FMT>(mats[m].scales, soff, row * spitch);
+      if constexpr (LANE_ROW) {
+        load_chunk<FMT>(mats[m].codes, coff + row * cpitch, 0, cw[i][m]);
+        sw[i][m] = load_scale<FMT>(mats[m].scales, soff + row * spitch, 0);
+      } else {
+        load_chunk<FMT>(mats[m].codes, coff, row * cpitch, cw[i][m]);
+        sw[i][m] = load_scale<FMT>(mats[m].scales, soff, row * spitch);
+      }
     }
   }
 }
@@ -402,19 +412,21 @@ __device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc
   const uint32_t coff = (uint32_t)(rg * cpitch + ch * F::CBYTES);
   const uint32_t soff = (uint32_t)(rg * spitch + ch * F::SBYTES);
   uint32_t cwa[R][2][F::CW], swa[R][2], cwb[R][2][F::CW], swb[R][2];
-  unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cwa, swa);
+  unit_load<FMT, 2, R, true>(mats, cpitch, spitch, tile * rw + up.rloc_u, geo.rpi, coff, soff, cwa,
+                             swa);
   uint32_t xr[GP][F::CB][VX][16];
   float ncr[GP][F::CB];
   load_prepared_x<FMT, GP, VX>(a, colidx, ch, xr, ncr);
   const uint32_t one = one_one_vgpr();
+  // the next unit's loads go out unconditionally; past the wave's last unit
+  // they address row f, outside the matrix, and read nothing
+  const int past = a.f;
   while (true) {
     {
       const int un = u + waves;
-      UnitPos upn{};
-      if (un < units) {
-        upn = unit_pos(un, P, R, geo.rpi);
-        unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + upn.rloc_u, geo.rpi, coff, soff, cwb, swb);
-      }
+      const UnitPos upn = unit_pos(un, P, R, geo.rpi);
+      unit_load<FMT, 2, R, true>(mats, cpitch, spitch, un < units ? tile * rw + upn.rloc_u : past,
+                                 geo.rpi, coff, soff, cwb, swb);
       float tot[R][2][GP];
       unit_compute<FMT, GP, VX, 2, R>(cwa, swa, xr, ncr, one, tot);
       gateup_reduce<FMT, GP, R>(tot, geo, up, c0, P, q, rw, gup);
@@ -424,11 +436,9 @@ __device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc
     }
     {
       const int un = u + waves;
-      UnitPos upn{};
-      if (un < units) {
-        upn = unit_pos(un, P, R, geo.rpi);
-        unit_load<FMT, 2, R>(mats, cpitch, spitch, tile * rw + upn.rloc_u, geo.rpi, coff, soff, cwa, swa);
-      }
+      const UnitPos upn = unit_pos(un, P, R, geo.rpi);
+      unit_load<FMT, 2, R, true>(mats, cpitch, spitch, un < units ? tile * rw + upn.rloc_u : past,
+                                 geo.rpi, coff, soff, cwa, swa);
       float tot[R][2][GP];
       unit_compute<FMT, GP, VX, 2, R>(cwb, swb, xr, ncr, one, tot);
       gateup_reduce<FMT, GP, R>(tot, geo, up, c0, P, q, rw, gup);
@@ -696,7 +706,7 @@ __device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, i
   uint32_t cwa[R][1][F::CW], swa[R][1], cwb[R][1][F::CW], swb[R][1];
   int u = u0;
   UnitPos up = unit_pos(u, P, R, geo.rpi);
-  unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + up.rloc_u, geo.rpi, coff, soff, cwa, swa);
+  unit_load<FMT, 1, R, true>(mats, cpitch, spitch, r0 + up.rloc_u, geo.rpi, coff, soff, cwa, swa);
   const uint32_t *hps = a.hp + (size_t)slot * a.q * a.nb_f * 32;
   const float *hncs = a.hnc + (size_t)slot * a.q * a.nb_f;
   uint32_t xr[GP][F::CB][2][16];
@@ -705,14 +715,15 @@ __device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, i
   const int col0 = sc.col(c0), col1 = GP == 2 ? sc.col(c0 + GP - 1) : col0;
   const float wgt0 = sc.weight(c0), wgt1 = GP == 2 ? sc.weight(c0 + GP - 1) : wgt0;
   const uint32_t one = one_one_vgpr();
+  // as in gateup_pass: the next unit's loads are unconditional, past the
+  // run they address row d, outside the matrix, and read nothing
+  const int past = a.d;
   while (true) {
     {
       const int un = u + 1;
-      UnitPos upn{};
-      if (un < u1) {
-        upn = unit_pos(un, P, R, geo.rpi);
-        unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + upn.rloc_u, geo.rpi, coff, soff, cwb, swb);
-      }
+      const UnitPos upn = unit_pos(un, P, R, geo.rpi);
+      unit_load<FMT, 1, R, true>(mats, cpitch, spitch, un < u1 ? r0 + upn.rloc_u : past, geo.rpi,
+                                 coff, soff, cwb, swb);
       float to[R][1][GP];
       unit_compute<FMT, GP, 2, 1, R>(cwa, swa, xr, ncr, one, to);
       down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
@@ -722,11 +733,9 @@ __device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, i
     }
     {
       const int un = u + 1;
-      UnitPos upn{};
-      if (un < u1) {
-        upn = unit_pos(un, P, R, geo.rpi);
-        unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + upn.rloc_u, geo.rpi, coff, soff, cwa, swa);
-      }
+      const UnitPos upn = unit_pos(un, P, R, geo.rpi);
+      unit_load<FMT, 1, R, true>(mats, cpitch, spitch, un < u1 ? r0 + upn.rloc_u : past, geo.rpi,
+                                 coff, soff, cwa, swa);
       float to[R][1][GP];
       unit_compute<FMT, GP, 2, 1, R>(cwb, swb, xr, ncr, one, to);
       down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
