@@ -270,7 +270,9 @@ def test_dense_host_checks(lib):
     assert fwd(q=0) == -2 and fwd(q=9) == -2 and fwd(rows=65) == -2
     assert fwd(fmt=7) == -4 and fwd(xt=2) == -1 and fwd(x=None) == -1
     assert fwd(img=C.c_void_p(0x1010)) == -3 and fwd(x=C.c_void_p(0x1008)) == -3
-    assert fwd(nbytes=8) == -5
+    # a tile split over several workgroups keeps partial sums in the workspace
+    assert lib.rfpx_dense_workspace_bytes(4, 64, 4096, 1) > 256
+    assert fwd(cols=4096, nbytes=256) == -5
     assert lib.rfpx_dense_image_build(4, p, 64, 256, p, 16, None) == -5
     assert lib.rfpx_dense_image_build(4, None, 64, 256, p, 1 << 20, None) == -1
 
