@@ -569,6 +569,47 @@ def bench_prefill(args, steps: int, warmup: int) -> dict:
     return out
 
 
+# -------------------------------------------------------------- plain read
+
+PLAIN_READ = "plain-read"
+# the packed bytes of one q=1 decode step: its down matrices, its gate/up
+# matrices, and all of them
+PLAIN_READ_SIZES = {"down_q1": 26476544, "gate_up_q1": 40370176, "step_q1": 66846720}
+
+
+def bench_plain_read(args, steps: int, warmup: int) -> dict:
+    """rfpx_stream_read (a plain streaming read, launch included) of the
+    byte counts the q=1 decode kernels stream, rotating over buffers that
+    total at least 512 MiB so that no read is served by the last-level
+    cache: the achievable ceiling each kernel is compared with."""
+    import torch
+
+    import block_quantized_expert_amd as bqe
+
+    dev = torch.device("cuda:0")
+    out = {"workload": PLAIN_READ, "steps": steps, "sizes": {}}
+    sink = torch.zeros(bqe.lib().rfpx_stream_read_sink_words(), dtype=torch.int32, device=dev)
+    for name, nbytes in PLAIN_READ_SIZES.items():
+        nbuf = max(2, -(-(512 << 20) // nbytes))
+        bufs = [torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+        for s in range(warmup):
+            bqe.rfpx_stream_read(bufs[s % nbuf], sink=sink)
+
+        def batch():
+            for s in range(steps):
+                bqe.rfpx_stream_read(bufs[s % nbuf], sink=sink)
+
+        us = [1e3 * b / steps for b in timed_batches(batch, BATCHES)]
+        med = statistics.median(us)
+        out["sizes"][name] = {"bytes": nbytes, "buffers_rotated": nbuf, "us_per_read": spread(us),
+                              "GB_per_s": nbytes / (med * 1e-6) / 1e9,
+                              "frac_of_peak": nbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------- dense
 
 DENSE_WORKLOAD = "dense-fp4-16384x4096"
@@ -650,7 +691,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
-                    choices=("all",) + DECODE_WORKLOADS + (PREFILL_WORKLOAD, DENSE_WORKLOAD))
+                    choices=("all",) + DECODE_WORKLOADS + (PREFILL_WORKLOAD, DENSE_WORKLOAD,
+                                                          PLAIN_READ))
     ap.add_argument("--layers", type=int, default=0,
                     help="layer instances to rotate over (default: the workload's rotation)")
     ap.add_argument("--variants", type=int, default=0,
@@ -683,6 +725,9 @@ def main() -> int:
                                       "weight_GB_per_s")})
         print(json.dumps(out))
         return 0
+    if args.workload == PLAIN_READ:
+        print(json.dumps(bench_plain_read(args, args.steps, args.warmup)))
+        return 0
     if args.workload == DENSE_WORKLOAD:
         print(json.dumps(bench_dense(args, args.steps, args.warmup)))
         return 0
@@ -708,6 +753,9 @@ def main() -> int:
     dense = bench_dense(args, args.steps, args.warmup)
     log(f"# {DENSE_WORKLOAD}: " + ", ".join(
         f"q={q} {v['us_per_call']['median']:.2f} us" for q, v in dense["q"].items()))
+    plain = bench_plain_read(args, args.steps, args.warmup)
+    log(f"# {PLAIN_READ}: " + ", ".join(
+        f"{k} {v['us_per_read']['median']:.2f} us" for k, v in plain["sizes"].items()))
     head = res[DECODE_WORKLOADS[0]]
     out = headline(head, args, METRIC)
     out["step_hbm"] = head["step_hbm"]
@@ -717,6 +765,15 @@ def main() -> int:
         slim = {k: v for k, v in w.items() if k not in ("config", "workload")}
         out["workloads"][name] = slim
     out["workloads"][DENSE_WORKLOAD] = dense
+    out["workloads"][PLAIN_READ] = plain
+    # each q=1 kernel against a plain read of the same bytes (launch included
+    # in both): the share of the achievable ceiling it reaches
+    ku = head["kernels_us"]
+    out["vs_plain_read"] = {
+        "k_gateup": plain["sizes"]["gate_up_q1"]["us_per_read"]["median"] / ku["k_gateup"],
+        "k_down": plain["sizes"]["down_q1"]["us_per_read"]["median"] / ku["k_down"],
+        "step": plain["sizes"]["step_q1"]["us_per_read"]["median"] / (head["ms_per_step"] * 1e3),
+    }
     print(json.dumps(out))
     return 0
 

@@ -37,6 +37,7 @@ SYMBOLS = (
     "moe_prefill_forward", "moe_prefill_forward_timed",
     "rfpx_dense_image_bytes", "rfpx_dense_image_build", "rfpx_dense_image_unpack",
     "rfpx_dense_workspace_bytes", "rfpx_dense_forward",
+    "rfpx_stream_read", "rfpx_stream_read_sink_words",
     "rfpx_status_str", "rfpx_last_error",
 )
 
@@ -104,6 +105,8 @@ def lib():
             "rfpx_dense_image_unpack": (I, [I, P, I, I, P, P]),
             "rfpx_dense_workspace_bytes": (S, [I, I, I, I]),
             "rfpx_dense_forward": (I, [I, P, I, I, P, I, I, P, P, S, P]),
+            "rfpx_stream_read": (I, [P, S, P, P]),
+            "rfpx_stream_read_sink_words": (S, []),
             "rfpx_status_str": (C.c_char_p, [I]),
             "rfpx_last_error": (C.c_char_p, []),
         }
@@ -449,6 +452,23 @@ def rfpx_dense_forward(m: DenseMatrix, x, y=None, ws=None, stream=None):
         m.fmt, _ptr(m.image), m.rows, m.cols, _ptr(x), _xtype(x), q, _ptr(y), _ptr(ws),
         ws.numel(), _stream(stream)))
     return y
+
+
+# ------------------------------------------------------------ measurement
+
+def rfpx_stream_read(buf, sink=None, stream=None):
+    """A plain streaming read of the cuda tensor buf (its bytes); returns the
+    sink tensor (int32 [rfpx_stream_read_sink_words()]), whose words XOR to
+    the XOR of buf's 32-bit words (words past the workgroup count are left
+    as they were: pass a zeroed sink to check)."""
+    import torch
+    _need_cuda(buf)
+    n = lib().rfpx_stream_read_sink_words()
+    if sink is None:
+        sink = torch.zeros(n, dtype=torch.int32, device=buf.device)
+    _check("rfpx_stream_read", lib().rfpx_stream_read(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+    return sink
 
 
 # ----------------------------------------------------------- convenience

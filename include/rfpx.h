@@ -322,6 +322,19 @@ rfpx_status rfpx_dense_forward(int fmt, const uint8_t *image_dev, int rows, int 
                                const void *x_dev, int xtype, int q, float *y_dev,
                                void *ws_dev, size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------- measurement
+ * A plain streaming read of bytes at src_dev (16-byte aligned, a non-zero
+ * multiple of 16 bytes): the achievable HBM ceiling for a read of that size,
+ * launch included, which the layer kernels are compared with ([P5]
+ * "新手常见疑问": decode is bound by memory bandwidth).  One kernel: eight
+ * 16-byte loads in flight per thread, at most rfpx_stream_read_sink_words()
+ * workgroups; workgroup w writes the XOR of the 32-bit words it read to
+ * sink_dev[w] (the XOR of all written words is the XOR of the buffer's
+ * words; sink_dev must hold rfpx_stream_read_sink_words() words). */
+rfpx_status rfpx_stream_read(const void *src_dev, size_t bytes, uint32_t *sink_dev,
+                             void *stream);
+size_t rfpx_stream_read_sink_words(void);
+
 const char *rfpx_status_str(int status);
 const char *rfpx_last_error(void);
 

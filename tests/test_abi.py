@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     declared = header_functions()
-    assert len(declared) == 25
+    assert len(declared) == 27
     assert set(declared) == set(bqe.SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
@@ -275,6 +275,16 @@ def test_dense_host_checks(lib):
     assert fwd(cols=4096, nbytes=256) == -5
     assert lib.rfpx_dense_image_build(4, p, 64, 256, p, 16, None) == -5
     assert lib.rfpx_dense_image_build(4, None, 64, 256, p, 1 << 20, None) == -1
+
+
+def test_stream_read_host_checks(lib):
+    p = C.c_void_p(0x1000)
+    assert lib.rfpx_stream_read_sink_words() == 2048
+    assert lib.rfpx_stream_read(None, 64, p, None) == -1
+    assert lib.rfpx_stream_read(p, 0, p, None) == -3
+    assert lib.rfpx_stream_read(p, 40, p, None) == -3
+    assert lib.rfpx_stream_read(C.c_void_p(0x1008), 64, p, None) == -3
+    assert lib.rfpx_stream_read(p, 64, C.c_void_p(0x2002), None) == -3
 
 
 def test_status_strings(lib):

@@ -44,7 +44,10 @@ def test_measured_traffic_follows_the_source_hash(tmp_path, monkeypatch):
 
 def test_source_hash_covers_every_kernel_source():
     csrc = os.path.join(ROOT, "block_quantized_expert_amd", "csrc")
-    kernels = {f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp")) and f != "codec.hip"}
+    # codec.hip (one-time packing and image build) and measure.hip (the plain
+    # read the kernels are compared with) hold no kernel a traffic summary covers
+    kernels = {f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp"))
+               and f not in ("codec.hip", "measure.hip")}
     assert kernels <= set(bench.KERNEL_SOURCES)
     assert len(bench.kernel_source_hash()) == 64
 

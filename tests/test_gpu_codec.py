@@ -210,3 +210,20 @@ def test_pack_weighted_full_matrix_bit_exact(bqe):
     got = bqe.rfpx_pack_weighted(2, torch.from_numpy(w).cuda(),
                                  torch.from_numpy(imp).cuda()).cpu().numpy()
     assert np.array_equal(got, oracle.pack_weighted(2, w, imp))
+
+
+# ------------------------------------------------------- plain read
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 26476544])
+def test_stream_read_reads_every_word(bqe, nbytes):
+    """rfpx_stream_read touches every 32-bit word once: the XOR of its sink
+    words is the XOR of the buffer's words (numpy), also for sizes that are
+    not a whole number of batches."""
+    import torch
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
+    buf = torch.from_numpy(host).cuda()
+    sink = bqe.rfpx_stream_read(buf)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(host.view(np.uint32))
