@@ -34,7 +34,10 @@
 // registers once for all columns of the pass (v_dot2 on the prepared
 // pairs), reduces each row across its lanes (DPP and permlane swaps) and
 // writes part sums to LDS.  Then h = silu(g) * u, and the workgroup prepares h for the down
-// matrix (bf16 hi + lo pair words) so k_down only loads it.
+// matrix (fp32, in the product order of the down format's exact-code decode,
+// CodeGroups in rfpx_impl.hpp) so k_down only loads it; k_down takes each
+// down code as its integer value (v_cvt_f32_ubyte) and adds c * h with fp32
+// FMAs.
 // Lane geometry (Geo): with a row of >= 64 chunks a wave covers one row per
 // step and lane l reads chunk l (+ 64 for the second part; fully coalesced
 // 1 KiB requests); shorter rows give each wave 64/cpl rows per step.
@@ -193,6 +196,65 @@ __device__ __forceinline__ void unit_compute(const uint32_t (&cw)[R][NM][Fmt<FMT
           tot[i][m][g] = fmaf(acc0 + acc1, s, tot[i][m][g]);
         }
       }
+    }
+  }
+}
+
+// The down products of one unit: the unit's rows against GP compact
+// columns of prepared h (fp32, in each block's product order, 32 values per
+// block and column), one exact-code FMA per weight and column (CodeGroups).
+// Rows are decoded one at a time, as in unit_compute.
+template <int FMT, int GP, int R>
+__device__ __forceinline__ void unit_compute_code(const uint32_t (&cw)[R][1][Fmt<FMT>::CW],
+                                                  const uint32_t (&sw)[R][1],
+                                                  const uint32_t (&xr)[GP][Fmt<FMT>::CB][2][16],
+                                                  const float (&ncr)[GP][Fmt<FMT>::CB],
+                                                  float (&tot)[R][1][GP]) {
+  using F = Fmt<FMT>;
+  using CG = CodeGroups<FMT>;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int g = 0; g < GP; ++g) tot[i][0][g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < F::CB; ++j) {
+      const uint32_t *w = &cw[i][0][j * F::BW];
+      const float s = block_scale<FMT>(block_scale_bits<FMT>(sw[i][0], j));
+      // two accumulators per column halve the chain of dependent FMAs
+      float acc[GP][2];
+#pragma unroll
+      for (int g = 0; g < GP; ++g) {
+        acc[g][0] = ncr[g][j];
+        acc[g][1] = 0.f;
+      }
+      static_for<CG::N>([&](auto GI) {
+        constexpr int gi = decltype(GI)::value;
+        constexpr CodeGroup cg = CG::g[gi];
+        uint32_t win;
+        if constexpr (cg.sh != 0)
+          win = __builtin_amdgcn_alignbit(w[cg.src + 1], w[cg.src], cg.sh);
+        else
+          win = w[cg.src];
+        uint32_t m = win & cg.mask;
+        // the masked word stays one value, so that each byte converts with
+        // v_cvt_f32_ubyte<b> instead of a byte extract of win plus a convert
+        asm("" : "+v"(m));
+        static_for<4>([&](auto B) {
+          constexpr int b = decltype(B)::value;
+          if constexpr (cg.b[b].j >= 0) {
+            constexpr int q = code_pos<FMT>(gi, b);
+            // v_cvt_f32_ubyte<b>: c * 2^k, exact
+            const float c = (float)((m >> (8 * b)) & 0xFFu);
+#pragma unroll
+            for (int g = 0; g < GP; ++g)
+              acc[g][q & 1] = fmaf(c, __uint_as_float(xr[g][j][q >> 4][q & 15]), acc[g][q & 1]);
+          }
+        });
+      });
+#pragma unroll
+      for (int g = 0; g < GP; ++g) tot[i][0][g] = fmaf(acc[g][0] + acc[g][1], s, tot[i][0][g]);
     }
   }
 }
@@ -537,7 +599,7 @@ __device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, 
       item = ((size_t)slot * a.q + ci) * a.nb_f + tile * nbt + bt;
       const float *hblk = hs + ci * a.rw_gu + 32 * bt;
       uint32_t *dst = a.hp + item * 32;
-      share = prep_h_pair_rt(fdn, hblk, p, dst);
+      share = prep_h_code_rt(fdn, hblk, p, reinterpret_cast<float *>(dst));
     }
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
@@ -681,7 +743,7 @@ __device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, 
   float ncr[GP][F::CB];
   load_prepared_h<FMT, GP>(hps, hncs, a.nb_f, c0, ch, xr, ncr);
   float to[R][1][GP];
-  unit_compute<FMT, GP, 2, 1, R>(cw, sw, xr, ncr, one_one_vgpr(), to);
+  unit_compute_code<FMT, GP, R>(cw, sw, xr, ncr, to);
   const int col0 = sc.col(c0), col1 = GP == 2 ? sc.col(c0 + GP - 1) : col0;
   const float wgt0 = sc.weight(c0), wgt1 = GP == 2 ? sc.weight(c0 + GP - 1) : wgt0;
   down_reduce<GP, R>(to, geo, up, a.rw_dn, col0, col1, wgt0, wgt1, accw);
@@ -725,7 +787,7 @@ __device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, i
       unit_load<FMT, 1, R, true>(mats, cpitch, spitch, un < u1 ? r0 + upn.rloc_u : past, geo.rpi,
                                  coff, soff, cwb, swb);
       float to[R][1][GP];
-      unit_compute<FMT, GP, 2, 1, R>(cwa, swa, xr, ncr, one, to);
+      unit_compute_code<FMT, GP, R>(cwa, swa, xr, ncr, to);
       down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
       u = un;
       up = upn;
@@ -737,7 +799,7 @@ __device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, i
       unit_load<FMT, 1, R, true>(mats, cpitch, spitch, un < u1 ? r0 + upn.rloc_u : past, geo.rpi,
                                  coff, soff, cwa, swa);
       float to[R][1][GP];
-      unit_compute<FMT, GP, 2, 1, R>(cwb, swb, xr, ncr, one, to);
+      unit_compute_code<FMT, GP, R>(cwb, swb, xr, ncr, to);
       down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
       u = un;
       up = upn;

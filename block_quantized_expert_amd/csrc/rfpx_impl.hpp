@@ -2,8 +2,10 @@
 // format constants, the device image and workspace layouts, the lane
 // geometry of the expert kernels, and the register-level block decode.
 //
-// Block decode on gfx950.  The expert products run on v_dot2c_f32_bf16
-// (two bf16 products added into an fp32 accumulator per lane per issue).
+// Block decode on gfx950.  The gate/up products (and prefill's operands)
+// run on v_dot2c_f32_bf16 (two bf16 products added into an fp32
+// accumulator per lane per issue); the decode kernels' down products use
+// the exact-code form further below (CodeGroups).
 // A packed code c is turned into a bf16 value by masking it into the
 // mantissa of 1.0 (0x3F80): a code whose lowest bit lands at mantissa bit k
 // gives 1 + c * 2^(k-7).  One v_and_or_b32 builds a pair word (two codes,
@@ -37,6 +39,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <utility>
 
 #include "../../include/rfpx.h"
 
@@ -147,7 +150,7 @@ struct WsLayout {
   size_t scores;    // fp32 [q][E]
   size_t xp;        // u32  [3 fmts][q][nb_d][vx][16]  prepared activations
   size_t xnc;       // fp32 [3][q][nb_d]               their accumulator starts
-  size_t hp;        // u32  [slots][q][nb_f][2][16]    prepared h (hi, lo)
+  size_t hp;        // fp32 [slots][q][nb_f][32]       prepared h (exact-code order)
   size_t hnc;       // fp32 [slots][q][nb_f]
   size_t total;
   int max_slots;
@@ -474,7 +477,7 @@ __device__ __forceinline__ void prep_pairs(const uint32_t *xb, uint32_t *pw, flo
   *nc = acc;
 }
 
-// One pair word of one block of h (fp32 values, split into bf16 hi + lo)
+// Prefill: one pair word of one block of h (fp32 values, split into bf16 hi + lo)
 // for a down matrix of format fmt (a runtime value): writes dst[p] (hi
 // parts) and dst[16 + p] (lo parts) and returns the pair's share of the
 // block's accumulator start.  A single code path for all formats: three
@@ -514,6 +517,216 @@ __device__ __forceinline__ float prep_h_pair_rt(int fmt, const float *hblk, int 
   dst[16 + p] = (__float_as_uint(ll * flo) >> 16) | (__float_as_uint(hl * fhi) & 0xFFFF0000u);
   return -((flo + o) * (lh + ll) + (fhi + o) * (hh + hl));
 }
+
+// ----------------------------------------- exact codes for the down products
+//
+// The decode kernels' down products take each code as its integer value:
+// the block's code dwords are masked so that every byte of a 32-bit window
+// holds at most one code, at bit k of the byte; v_cvt_f32_ubyte turns the
+// byte into c * 2^k exactly, the prepared h carries the factor 2^-k, and an
+// fp32 FMA adds c * h.  The block sum starts at -o * sum(h), so it ends at
+// sum_j (c_j - o) h_j.  Per weight and column this is one FMA (plus the
+// convert, shared by the columns), where a bf16 hi + lo h costs two bf16
+// dot products per pair of weights; on this device an fp32 FMA or byte
+// convert issues at twice the rate of a v_dot2.
+//
+// A group is a 32-bit window of the block's code dwords (dword `src`, or
+// alignbit(w[src + 1], w[src], sh) when sh != 0), the mask applied to it,
+// and for each byte the code it holds and that code's bit k in the byte (j
+// < 0: no code).  Codes sit at bits 2j (FP2), 3j (FP3) or 4j (FP4) of the
+// block's little-endian code word.  The products run group by group, byte
+// by byte, and the prepared h of a block is stored in that order.
+struct CodeByte {
+  int8_t j, k;
+};
+struct CodeGroup {
+  int8_t src, sh;
+  uint32_t mask;
+  CodeByte b[4];
+};
+
+template <int FMT>
+struct CodeGroups;
+
+// FP2: per dword t, mask 0x03030303 << 2u keeps the codes 16t + 4i + u.
+template <>
+struct CodeGroups<RFPX_FP2> {
+  static constexpr int N = 8;
+  static constexpr CodeGroup g[N] = {
+      {0, 0, 0x03030303u, {{0, 0}, {4, 0}, {8, 0}, {12, 0}}},
+      {0, 0, 0x0C0C0C0Cu, {{1, 2}, {5, 2}, {9, 2}, {13, 2}}},
+      {0, 0, 0x30303030u, {{2, 4}, {6, 4}, {10, 4}, {14, 4}}},
+      {0, 0, 0xC0C0C0C0u, {{3, 6}, {7, 6}, {11, 6}, {15, 6}}},
+      {1, 0, 0x03030303u, {{16, 0}, {20, 0}, {24, 0}, {28, 0}}},
+      {1, 0, 0x0C0C0C0Cu, {{17, 2}, {21, 2}, {25, 2}, {29, 2}}},
+      {1, 0, 0x30303030u, {{18, 4}, {22, 4}, {26, 4}, {30, 4}}},
+      {1, 0, 0xC0C0C0C0u, {{19, 6}, {23, 6}, {27, 6}, {31, 6}}},
+  };
+};
+
+// FP3: codes 3j never share a byte boundary pattern with the bytes of one
+// window, so the 32 codes come from six masks on the three dwords and
+// three masks on windows shifted by 2, 34 and 58 bits (twelve integer
+// operations per block).
+template <>
+struct CodeGroups<RFPX_FP3> {
+  static constexpr int N = 9;
+  static constexpr CodeGroup g[N] = {
+      {0, 0, 0x071C0E07u, {{0, 0}, {3, 1}, {6, 2}, {8, 0}}},
+      {0, 0, 0x38E07038u, {{1, 3}, {4, 4}, {7, 5}, {9, 3}}},
+      {1, 0, 0x0E071C0Eu, {{11, 1}, {14, 2}, {16, 0}, {19, 1}}},
+      {1, 0, 0x7038E070u, {{12, 4}, {15, 5}, {17, 3}, {20, 4}}},
+      {2, 0, 0x1C0E071Cu, {{22, 2}, {24, 0}, {27, 1}, {30, 2}}},
+      {2, 0, 0xE07038E0u, {{23, 5}, {25, 3}, {28, 4}, {31, 5}}},
+      {0, 2, 0x7000E070u, {{2, 4}, {5, 5}, {-1, 0}, {10, 4}}},
+      {1, 2, 0xE07000E0u, {{13, 5}, {-1, 0}, {18, 4}, {21, 5}}},
+      {1, 26, 0xE0700000u, {{-1, 0}, {-1, 0}, {26, 4}, {29, 5}}},
+  };
+};
+
+// FP4: per dword t, mask 0x0F0F0F0F keeps the codes 8t + 2i, 0xF0F0F0F0
+// the codes 8t + 2i + 1.
+template <>
+struct CodeGroups<RFPX_FP4> {
+  static constexpr int N = 8;
+  static constexpr CodeGroup g[N] = {
+      {0, 0, 0x0F0F0F0Fu, {{0, 0}, {2, 0}, {4, 0}, {6, 0}}},
+      {0, 0, 0xF0F0F0F0u, {{1, 4}, {3, 4}, {5, 4}, {7, 4}}},
+      {1, 0, 0x0F0F0F0Fu, {{8, 0}, {10, 0}, {12, 0}, {14, 0}}},
+      {1, 0, 0xF0F0F0F0u, {{9, 4}, {11, 4}, {13, 4}, {15, 4}}},
+      {2, 0, 0x0F0F0F0Fu, {{16, 0}, {18, 0}, {20, 0}, {22, 0}}},
+      {2, 0, 0xF0F0F0F0u, {{17, 4}, {19, 4}, {21, 4}, {23, 4}}},
+      {3, 0, 0x0F0F0F0Fu, {{24, 0}, {26, 0}, {28, 0}, {30, 0}}},
+      {3, 0, 0xF0F0F0F0u, {{25, 4}, {27, 4}, {29, 4}, {31, 4}}},
+  };
+};
+
+// Every group's mask keeps exactly the listed codes at the listed bits, and
+// the groups together list each of the block's 32 codes once.
+template <int FMT>
+constexpr bool code_groups_valid() {
+  constexpr int bits = FMT == RFPX_FP2 ? 2 : FMT == RFPX_FP3 ? 3 : 4;
+  bool seen[32] = {};
+  int n = 0;
+  for (int gi = 0; gi < CodeGroups<FMT>::N; ++gi) {
+    const CodeGroup &g = CodeGroups<FMT>::g[gi];
+    const int s = 32 * g.src + g.sh;
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t bm = (g.mask >> (8 * b)) & 0xFFu;
+      if (g.b[b].j < 0) {
+        if (bm != 0) return false;
+        continue;
+      }
+      const int j = g.b[b].j, k = g.b[b].k;
+      if (j >= 32 || seen[j] || bits * j - s - 8 * b != k) return false;
+      if (bm != (((1u << bits) - 1u) << k)) return false;
+      seen[j] = true;
+      ++n;
+    }
+  }
+  return n == 32;
+}
+static_assert(code_groups_valid<RFPX_FP2>(), "FP2 code groups");
+static_assert(code_groups_valid<RFPX_FP3>(), "FP3 code groups");
+static_assert(code_groups_valid<RFPX_FP4>(), "FP4 code groups");
+
+// The code and bit of product position q (0..31) of a block.
+template <int FMT>
+constexpr CodeByte code_at(int q) {
+  for (int gi = 0, n = 0; gi < CodeGroups<FMT>::N; ++gi)
+    for (int b = 0; b < 4; ++b)
+      if (CodeGroups<FMT>::g[gi].b[b].j >= 0 && n++ == q) return CodeGroups<FMT>::g[gi].b[b];
+  return CodeByte{-1, 0};
+}
+
+// The same order in closed form for FP2 (group g = 4t + u holds codes 16t +
+// 4i + u at bit 2u) and FP4 (group g = 2t + odd holds codes 8t + 2i + odd at
+// bit 4 odd); position q = 4g + i.
+__host__ __device__ constexpr CodeByte code_fp2(int q) {
+  return CodeByte{(int8_t)(16 * (q >> 4) + 4 * (q & 3) + ((q >> 2) & 3)), (int8_t)(2 * ((q >> 2) & 3))};
+}
+__host__ __device__ constexpr CodeByte code_fp4(int q) {
+  return CodeByte{(int8_t)(8 * (q >> 3) + 2 * (q & 3) + ((q >> 2) & 1)), (int8_t)(4 * ((q >> 2) & 1))};
+}
+constexpr bool closed_forms_match() {
+  for (int q = 0; q < 32; ++q) {
+    if (code_fp2(q).j != code_at<RFPX_FP2>(q).j || code_fp2(q).k != code_at<RFPX_FP2>(q).k) return false;
+    if (code_fp4(q).j != code_at<RFPX_FP4>(q).j || code_fp4(q).k != code_at<RFPX_FP4>(q).k) return false;
+  }
+  return true;
+}
+static_assert(closed_forms_match(), "closed-form product order");
+
+// Product position of byte b of group gi (the number of codes before it).
+template <int FMT>
+constexpr int code_pos(int gi, int b) {
+  int n = 0;
+  for (int g = 0; g < CodeGroups<FMT>::N; ++g)
+    for (int bb = 0; bb < 4; ++bb) {
+      if (g == gi && bb == b) return n;
+      if (CodeGroups<FMT>::g[g].b[bb].j >= 0) ++n;
+    }
+  return -1;
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, expanded at compile
+// time (so that table entries indexed by I are constants).
+template <typename F, int... I>
+__host__ __device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__host__ __device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// The product order of a block as two bytes per position (code, bit), for
+// a runtime lookup.
+template <int FMT>
+struct CodeOrder {
+  uint8_t j[32], k[32];
+  constexpr CodeOrder() : j(), k() {
+    for (int q = 0; q < 32; ++q) {
+      j[q] = (uint8_t)code_at<FMT>(q).j;
+      k[q] = (uint8_t)code_at<FMT>(q).k;
+    }
+  }
+};
+
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+// Prepared h of one block of a down matrix of format fmt (a runtime
+// value), two product positions per lane (p and p + 16 of the block's 16
+// lanes): dst[q] = h[code_at(q).j] * 2^-code_at(q).k.  Returns the lane's
+// share of the block's accumulator start, -o times its two h values.
+__device__ __forceinline__ float prep_h_code_rt(int fmt, const float *hblk, int p, float *dst) {
+  int j0, k0, j1, k1;
+  float o;
+  if (fmt == RFPX_FP2) {
+    j0 = code_fp2(p).j;
+    k0 = code_fp2(p).k;
+    j1 = code_fp2(p + 16).j;
+    k1 = code_fp2(p + 16).k;
+    o = 1.5f;
+  } else if (fmt == RFPX_FP4) {
+    j0 = code_fp4(p).j;
+    k0 = code_fp4(p).k;
+    j1 = code_fp4(p + 16).j;
+    k1 = code_fp4(p + 16).k;
+    o = 7.5f;
+  } else {
+    constexpr CodeOrder<RFPX_FP3> ord{};
+    j0 = ord.j[p];
+    k0 = ord.k[p];
+    j1 = ord.j[p + 16];
+    k1 = ord.k[p + 16];
+    o = 3.5f;
+  }
+  const float h0 = hblk[j0], h1 = hblk[j1];
+  dst[p] = h0 * __uint_as_float((uint32_t)(127 - k0) << 23);
+  dst[p + 16] = h1 * __uint_as_float((uint32_t)(127 - k1) << 23);
+  return -o * (h0 + h1);
+}
+#endif
 
 // Block scale as an fp32 multiplier: fp16 bits (FP2/FP3) or E8M0 (FP4).
 template <int FMT>
