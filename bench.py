@@ -550,6 +550,7 @@ def bench_prefill(args, steps: int, warmup: int) -> dict:
         "useful_gflop": flops / 1e9,
         "mfma_utilization": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
         "kernels_us": st,
+        "kernels_bytes": {k: v[2] for k, v in products.items()},
         "roofline": {"bound": "mfma", "achieved": tfl, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tfl / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": measured_traffic(dom, name),
@@ -722,7 +723,7 @@ def main() -> int:
         out = headline(w, args, "MoE-layer prefill tokens/s (2048-token chunk) and MFMA "
                                 "utilization")
         out.update({k: w[k] for k in ("useful_gflop", "mfma_utilization", "kernels_us",
-                                      "weight_GB_per_s")})
+                                      "kernels_bytes", "weight_GB_per_s")})
         print(json.dumps(out))
         return 0
     if args.workload == PLAIN_READ:
