@@ -220,6 +220,10 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
       }
     const int units = (L->top_k + 1) * per_slot;
     if (units < p->wmax) p->wmax = (units + parts - 1) / parts * parts;
+    // one unit per slot and one wave per slot: a wave knows its slot (and,
+    // with one block per lane, its h) before the route table arrives
+    p->h_early = per_slot == 1 && parts == 1 && p->wmax == L->top_k + 1 &&
+                 !((p->down_fmts >> RFPX_FP2) & 1u);
   }
   while (p->wmax > 2 && (size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024) p->wmax /= 2;
   if ((size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024)

@@ -58,6 +58,7 @@ struct ExpArgs {
   int d, f, q, nb_d, nb_f;
   int rw_gu, rw_dn;
   Geo geo_gu[5], geo_dn[5];  // by format; all zero for a format not in the host table
+  int h_early;               // k_down<1>: see ForwardPlan::h_early
 };
 
 // A format read from the device table that the launch was planned for: the
@@ -749,6 +750,34 @@ __device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, 
   down_reduce<GP, R>(to, geo, up, a.rw_dn, col0, col1, wgt0, wgt1, accw);
 }
 
+// The only unit of a slot's down matrix in a one-column step (rows r0 ..
+// r0 + R of the tile, part 0), with the slot's prepared h already in
+// registers (FP3/FP4: one block per lane): weights, products, and the
+// weighted row results into the wave's accumulator rows.
+template <int FMT>
+__device__ __forceinline__ void down_unit_h(const ExpArgs &a, uint64_t codes, uint64_t scales,
+                                            int r0, int col0, float wgt,
+                                            const uint32_t (&hx)[1][1][2][16],
+                                            const float (&hn)[1][1], float *accw) {
+  using F = Fmt<FMT>;
+  static_assert(F::CB == 1, "one block per lane");
+  constexpr int R = unit_rows_for(FMT, 1);
+  const Geo geo = a.geo_dn[FMT];
+  const uint32_t cpitch = (uint32_t)(a.f / 32) * code_bytes(FMT);
+  const uint32_t spitch = (uint32_t)(a.f / 32) * scale_bytes(FMT);
+  const MatPtr mats[1] = {{make_rsrc(a.image + codes, a.d * cpitch), make_rsrc(a.image + scales, a.d * spitch)}};
+  const int lane = threadIdx.x & 63;
+  const int rg = lane / geo.lpr, li = lane % geo.lpr;
+  const uint32_t coff = (uint32_t)(rg * cpitch + li * F::CBYTES);
+  const uint32_t soff = (uint32_t)(rg * spitch + li * F::SBYTES);
+  uint32_t cw[R][1][F::CW], sw[R][1];
+  unit_load<FMT, 1, R>(mats, cpitch, spitch, r0, geo.rpi, coff, soff, cw, sw);
+  float to[R][1][1];
+  unit_compute_code<FMT, 1, R>(cw, sw, hx, hn, to);
+  const UnitPos up = unit_pos(0, 1, R, geo.rpi);
+  down_reduce<1, R>(to, geo, up, a.rw_dn, col0, col0, wgt, wgt, accw);
+}
+
 // Units [u0, u1) of one slot's down matrix for GP compact columns c0..,
 // all in column part 0: the wave loads the slot's prepared h of its chunk
 // once and streams the units with the next unit's code and scale loads in
@@ -889,6 +918,21 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
   // table loads need not wait for the slot count
   const int nslots = G == 1 ? a.rp.k + 1 : uniform(a.rt->nslots);
   for (int i = threadIdx.x; i < waves * q * rw; i += blockDim.x) acc[i] = 0.f;
+  // One-column steps with one unit per slot and one wave per slot: wave w's
+  // unit is slot w's, and its prepared h (one block per lane, 32 words) does
+  // not depend on the route table.  Waves other than the table reader's
+  // load it before the table is read, the table reader right after, so
+  // that h is not in flight with the weights.
+  const bool early = G == 1 && a.h_early;
+  uint32_t hx[1][1][2][16];
+  float hn[1][1];
+  // the lane's block: FP3 and FP4 chunks are one block, so both formats
+  // give a row of nb_f chunks <= 64 lanes (one column part), lane l block
+  // l mod nb_f
+  const int hch = (threadIdx.x & 63) % (a.nb_f < 64 ? a.nb_f : 64);
+  if (early && wave != 0 && wave < nslots)
+    load_prepared_h<RFPX_FP4, 1>(a.hp + (size_t)wave * a.nb_f * 32, a.hnc + (size_t)wave * a.nb_f,
+                                 a.nb_f, 0, hch, hx, hn);
   // the slot table and each slot's down-matrix entry of the image table,
   // all loads in flight together
   for (int i = threadIdx.x; i < nslots * (kQMax + 1); i += blockDim.x) {
@@ -906,9 +950,22 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
       t_w[s][j] = a.rt->w[s][j];
     }
   }
+  if (early && wave == 0) load_prepared_h<RFPX_FP4, 1>(a.hp, a.hnc, a.nb_f, 0, hch, hx, hn);
   __syncthreads();
   const int r0 = blockIdx.x * rw;
   float *accw = acc + wave * q * rw;
+  if (early) {
+    if (wave < nslots) {
+      const int fmt = uniform(t_fmt[wave]);
+      const int col0 = uniform(t_cols[wave][0]);
+      const float wgt = __int_as_float(uniform(__float_as_int(t_w[wave][0])));
+      const uint64_t codes = uniform64(t_codes[wave]), scales = uniform64(t_scales[wave]);
+      if (fmt == RFPX_FP3)
+        down_unit_h<RFPX_FP3>(a, codes, scales, r0, col0, wgt, hx, hn, accw);
+      else if (fmt == RFPX_FP4)
+        down_unit_h<RFPX_FP4>(a, codes, scales, r0, col0, wgt, hx, hn, accw);
+    }
+  }
   // Steps of several columns: the units of all slots in slot order, cut
   // into one contiguous run per wave (a run keeps a slot's h in registers
   // across its units); needs every down format in one column part.
@@ -948,7 +1005,7 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
     }
   }
   int item = 0;
-  for (int s = 0; s < nslots && !runs; ++s) {
+  for (int s = 0; s < nslots && !runs && !early; ++s) {
     SlotCols sc;
     sc.expert = -1;  // not needed: the down entry is in LDS
     sc.ncols = uniform(t_ncols[s]);
@@ -992,6 +1049,7 @@ ExpArgs make_args(const ForwardPlan &p) {
   }
   a.rw_gu = p.rw_gu;
   a.rw_dn = p.rw_dn;
+  a.h_early = p.h_early ? 1 : 0;
   return a;
 }
 

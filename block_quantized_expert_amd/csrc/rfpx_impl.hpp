@@ -810,6 +810,8 @@ struct ForwardPlan {
   int rw_gu, rw_dn;         // rows per workgroup tile
   bool route_only;
   bool pre_route;           // the routing step runs once (k_topk) before the experts
+  bool h_early;             // k_down<1>: wave w owns slot w's only unit and loads its
+                            // h while the route table is read (no FP2 down matrices)
   hipStream_t stream;
   // optional, 6 hipEvent_t: start and end of the routing kernels, of the
   // gate/up kernel and of the down kernel
