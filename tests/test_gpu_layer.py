@@ -193,6 +193,10 @@ def test_wide_router_shared_experts(bqe):
     assert len(set(cols.drawn.reshape(-1).tolist())) < 64
     y_ref, _, _ = _oracle(lay, cols.x, "bf16")
     assert_close(_run(bqe, L, cols.x), y_ref, what="E=1024 k=8 q=8")
+    # one column: the routing step reads the chosen experts' entries from
+    # the image, since a table this wide is not copied to LDS
+    y1, _, _ = _oracle(lay, cols.x[:1], "bf16")
+    assert_close(_run(bqe, L, cols.x[:1]), y1, what="E=1024 k=8 q=1")
 
 
 # ---------------------------------------- decode size, d=4096, f=2048, E=256
