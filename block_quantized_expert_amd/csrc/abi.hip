@@ -225,8 +225,9 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
     p->h_early = per_slot == 1 && parts == 1 && p->wmax == L->top_k + 1 &&
                  !((p->down_fmts >> RFPX_FP2) & 1u);
   }
-  while (p->wmax > 2 && (size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024) p->wmax /= 2;
-  if ((size_t)p->wmax * q * p->rw_dn * sizeof(float) > 48 * 1024)
+  // per wave: its accumulator rows and 64 sink words
+  while (p->wmax > 2 && (size_t)p->wmax * (q * p->rw_dn + 64) * sizeof(float) > 48 * 1024) p->wmax /= 2;
+  if ((size_t)p->wmax * (q * p->rw_dn + 64) * sizeof(float) > 48 * 1024)
     return fail(RFPX_E_SHAPE, "f=%d, q=%d: down tile of %d rows needs too much LDS", L->f, q,
                 p->rw_dn);
 

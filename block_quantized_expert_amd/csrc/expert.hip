@@ -370,6 +370,17 @@ __device__ __forceinline__ UnitPos unit_pos(int u, int parts, int r, int rpi) {
   return up;
 }
 
+// Dynamic LDS of the product kernels.  Its first blockDim.x words are a
+// sink: one word per thread that a reduction's non-writer lanes store to,
+// so that the stores of a unit's results need no branch on the lane.  A
+// lane-dependent branch inside a unit loop makes the compiler treat the
+// loop's exits as divergent, and the extra control-flow path it then adds
+// to the loop head makes the next unit's loads wait for every load in
+// flight, which undoes the double buffering.
+extern __shared__ float dyn_lds[];
+
+__device__ __forceinline__ float *lane_sink() { return dyn_lds + threadIdx.x; }
+
 // ------------------------------------------------------------ gate / up
 
 // Part sums of one computed unit to LDS: gup[m][part][column][row].
@@ -395,10 +406,11 @@ __device__ __forceinline__ void gateup_reduce(const float (&tot)[R][2][GP], cons
         for (int g = 0; g < GP; ++g) flat[(i * 2 + m) * GP + g] = tot[i][m][g];
     const float v = multi_sum<NP>(flat, lane);
     const int n = ms_index<NP>(lane);
-    if (ms_writer<NP>(lane) && n < N) {
-      const int i = n / (2 * GP), m = (n / GP) % 2, g = n % GP;
-      gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + i] = v;
-    }
+    const int i = n / (2 * GP), m = (n / GP) % 2, g = n % GP;
+    float *dst = ms_writer<NP>(lane) && n < N
+                     ? &gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + i]
+                     : lane_sink();
+    *dst = v;
   } else {
 #pragma unroll
     for (int i = 0; i < R; ++i)
@@ -407,8 +419,9 @@ __device__ __forceinline__ void gateup_reduce(const float (&tot)[R][2][GP], cons
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
           const float v = group_sum(tot[i][m][g], geo.lpr);
-          if (li == 0)
-            gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i] = v;
+          float *dst = li == 0 ? &gup[((m * P + up.part) * q + c0 + g) * rw + up.rloc_u + rg + geo.rpi * i]
+                               : lane_sink();
+          *dst = v;
         }
   }
 }
@@ -482,20 +495,23 @@ __device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc
   load_prepared_x<FMT, GP, VX>(a, colidx, ch, xr, ncr);
   const uint32_t one = one_one_vgpr();
   // the next unit's loads go out unconditionally; past the wave's last unit
-  // they address row f, outside the matrix, and read nothing
+  // they address row f, outside the matrix, and read nothing.  Units go in
+  // pairs (set a, then set b) with the loop's only exit at its head, and an
+  // odd last unit after it: an exit between the two halves would add a path
+  // into the loop head on which set b's loads are still in flight, and the
+  // compiler would then wait for every load there, each iteration
   const int past = a.f;
-  while (true) {
+  while (u + waves < units) {
     {
       const int un = u + waves;
       const UnitPos upn = unit_pos(un, P, R, geo.rpi);
-      unit_load<FMT, 2, R, true>(mats, cpitch, spitch, un < units ? tile * rw + upn.rloc_u : past,
-                                 geo.rpi, coff, soff, cwb, swb);
+      unit_load<FMT, 2, R, true>(mats, cpitch, spitch, tile * rw + upn.rloc_u, geo.rpi, coff, soff,
+                                 cwb, swb);
       float tot[R][2][GP];
       unit_compute<FMT, GP, VX, 2, R>(cwa, swa, xr, ncr, one, tot);
       gateup_reduce<FMT, GP, R>(tot, geo, up, c0, P, q, rw, gup);
       u = un;
       up = upn;
-      if (u >= units) break;
     }
     {
       const int un = u + waves;
@@ -507,8 +523,12 @@ __device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc
       gateup_reduce<FMT, GP, R>(tot, geo, up, c0, P, q, rw, gup);
       u = un;
       up = upn;
-      if (u >= units) break;
     }
+  }
+  if (u < units) {
+    float tot[R][2][GP];
+    unit_compute<FMT, GP, VX, 2, R>(cwa, swa, xr, ncr, one, tot);
+    gateup_reduce<FMT, GP, R>(tot, geo, up, c0, P, q, rw, gup);
   }
 }
 
@@ -617,7 +637,7 @@ template <int G, int VX>
 __global__ __launch_bounds__(512) void k_gateup(ExpArgs a) {
   const int slot = blockIdx.y;
   __shared__ RouteLds rs;
-  extern __shared__ float lds[];
+  float *lds = dyn_lds + blockDim.x;  // past the sink
   SlotCols sc;
   if (slot == 0) {
     if (threadIdx.x < kQMax) {
@@ -704,20 +724,19 @@ __device__ __forceinline__ void down_reduce(const float (&to)[R][1][GP], const G
 #pragma unroll
       for (int g = 0; g < GP; ++g) flat[i * GP + g] = to[i][0][g];
     const float v = multi_sum<N>(flat, lane);
-    if (ms_writer<N>(lane)) {
-      const int n = ms_index<N>(lane);
-      const int i = n / GP, g = n % GP;
-      const int cg = (GP == 2 && g) ? col1 : col0;
-      const float wg = (GP == 2 && g) ? wgt1 : wgt0;
-      lds_add(&accw[cg * rw + up.rloc_u + i], wg * v);
-    }
+    const int n = ms_index<N>(lane);
+    const int i = n / GP, g = n % GP;
+    const int cg = (GP == 2 && g) ? col1 : col0;
+    const float wg = (GP == 2 && g) ? wgt1 : wgt0;
+    lds_add(ms_writer<N>(lane) ? &accw[cg * rw + up.rloc_u + i] : lane_sink(), wg * v);
   } else {
 #pragma unroll
     for (int g = 0; g < GP; ++g)
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         const float v = group_sum(to[i][0][g], geo.lpr);
-        if (li == 0) lds_add(&accw[(g ? col1 : col0) * rw + up.rloc_u + rg + geo.rpi * i], (g ? wgt1 : wgt0) * v);
+        lds_add(li == 0 ? &accw[(g ? col1 : col0) * rw + up.rloc_u + rg + geo.rpi * i] : lane_sink(),
+                (g ? wgt1 : wgt0) * v);
       }
   }
 }
@@ -806,21 +825,20 @@ __device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, i
   const int col0 = sc.col(c0), col1 = GP == 2 ? sc.col(c0 + GP - 1) : col0;
   const float wgt0 = sc.weight(c0), wgt1 = GP == 2 ? sc.weight(c0 + GP - 1) : wgt0;
   const uint32_t one = one_one_vgpr();
-  // as in gateup_pass: the next unit's loads are unconditional, past the
-  // run they address row d, outside the matrix, and read nothing
+  // as in gateup_pass: the next unit's loads are unconditional (past the
+  // run they address row d, outside the matrix, and read nothing), units go
+  // in pairs with the loop's only exit at its head, an odd last one after
   const int past = a.d;
-  while (true) {
+  while (u + 1 < u1) {
     {
       const int un = u + 1;
       const UnitPos upn = unit_pos(un, P, R, geo.rpi);
-      unit_load<FMT, 1, R, true>(mats, cpitch, spitch, un < u1 ? r0 + upn.rloc_u : past, geo.rpi,
-                                 coff, soff, cwb, swb);
+      unit_load<FMT, 1, R, true>(mats, cpitch, spitch, r0 + upn.rloc_u, geo.rpi, coff, soff, cwb, swb);
       float to[R][1][GP];
       unit_compute_code<FMT, GP, R>(cwa, swa, xr, ncr, to);
       down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
       u = un;
       up = upn;
-      if (u >= u1) break;
     }
     {
       const int un = u + 1;
@@ -832,8 +850,12 @@ __device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, i
       down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
       u = un;
       up = upn;
-      if (u >= u1) break;
     }
+  }
+  if (u < u1) {
+    float to[R][1][GP];
+    unit_compute_code<FMT, GP, R>(cwa, swa, xr, ncr, to);
+    down_reduce<GP, R>(to, geo, up, rw, col0, col1, wgt0, wgt1, accw);
   }
 }
 
@@ -910,7 +932,7 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
   __shared__ float t_w[kMaxSlots][kQMax];
   __shared__ uint64_t t_codes[kMaxSlots], t_scales[kMaxSlots];
   __shared__ int32_t t_fmt[kMaxSlots];
-  extern __shared__ float acc[];  // [waves][q][rw]
+  float *acc = dyn_lds + blockDim.x;  // [waves][q][rw], past the sink
   const int rw = a.rw_dn, q = a.q;
   const int waves = blockDim.x >> 6;
   const int wave = uniform(threadIdx.x >> 6);
@@ -1058,9 +1080,9 @@ ExpArgs make_args(const ForwardPlan &p) {
 hipError_t launch_experts(const ForwardPlan &p) {
   const ExpArgs a = make_args(p);
   const dim3 ggu(p.f / p.rw_gu, p.wl.max_slots), gdn(p.d / p.rw_dn);
-  const size_t lds_gu = (size_t)5 * p.q * p.rw_gu * sizeof(float);        // hs + gup
-  const size_t lds_dn = (size_t)p.wmax * p.q * p.rw_dn * sizeof(float);   // acc
   const unsigned nt = 64 * p.wmax, ntg = 64 * p.wgu;
+  const size_t lds_gu = ((size_t)ntg + 5 * p.q * p.rw_gu) * sizeof(float);          // sink + hs + gup
+  const size_t lds_dn = ((size_t)nt + (size_t)p.wmax * p.q * p.rw_dn) * sizeof(float);  // sink + acc
   const bool bf = p.xtype == RFPX_X_BF16;
   hipEvent_t *ev = (hipEvent_t *)p.events;
   hipEvent_t e0 = ev ? ev[2] : nullptr, e1 = ev ? ev[3] : nullptr;
