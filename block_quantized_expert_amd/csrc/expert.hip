@@ -1002,13 +1002,31 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
     return fmt == RFPX_FP2 ? ups2 : fmt == RFPX_FP3 ? ups3 : fmt == RFPX_FP4 ? ups4 : 0;
   };
   if (runs) {
-    int total = 0;
-    for (int s = 0; s < nslots; ++s) total += slot_units(uniform(t_fmt[s]));
+    // The wave finds its run without walking the table slot by slot (one
+    // LDS read and wait per slot, before the first weight load): lane l
+    // takes slot l's unit count (slot 64, the last possible one, is read
+    // apart), a wave scan gives the prefix sums, a ballot the first slot
+    // that reaches into the run, and each slot's start and count are then
+    // read from the scan's lanes.
+    const int l = threadIdx.x & 63;
+    const int cl = l < nslots ? slot_units(t_fmt[l]) : 0;
+    int inc = cl;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(inc, off, 64);
+      inc += l >= off ? v : 0;
+    }
+    const int c64 = nslots > 64 ? slot_units(uniform(t_fmt[64])) : 0;
+    const int tot64 = __builtin_amdgcn_readlane(inc, 63);
+    const int total = tot64 + c64;
     const int lo = total * wave / waves, hi = total * (wave + 1) / waves;
-    int start = 0;
-    for (int s = 0; s < nslots && start < hi; ++s) {
+    // slots that end at or before the run's start
+    int s = __popcll(__ballot(l < nslots && inc <= lo));
+    for (; s < nslots; ++s) {
+      const int ups = s < 64 ? __builtin_amdgcn_readlane(cl, s) : c64;
+      const int start = s < 64 ? __builtin_amdgcn_readlane(inc, s) - ups : tot64;
+      if (start >= hi) break;
       const int fmt = uniform(t_fmt[s]);
-      const int ups = slot_units(fmt);
       const int u0 = lo > start ? lo - start : 0, u1 = hi < start + ups ? hi - start : ups;
       if (u0 < u1) {
         SlotCols sc;
@@ -1023,7 +1041,6 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
         else if (fmt == RFPX_FP3) down_slot_run<RFPX_FP3, G>(a, sc, s, ed, r0, u0, u1, accw);
         else down_slot_run<RFPX_FP4, G>(a, sc, s, ed, r0, u0, u1, accw);
       }
-      start += ups;
     }
   }
   int item = 0;

@@ -199,6 +199,23 @@ def test_wide_router_shared_experts(bqe):
     assert_close(_run(bqe, L, cols.x[:1]), y1, what="E=1024 k=8 q=1")
 
 
+def test_sixty_five_slots(bqe, monkeypatch):
+    """q = 8 columns steered to disjoint top-8 sets over E = 64 experts: 64
+    routed slots plus the shared one, the most a step can hold; the down
+    kernel's waves find their runs from a 64-lane scan of the slots' unit
+    counts, with the 65th slot's count taken apart."""
+    cfg = synth.Config("slots65", 512, 128, 64, 8, 8, "bf16", "zipf", scale_floor=1e-3,
+                       master=4242)
+    lay = synth.gen_layer(cfg, 0, threads=4)
+    sets = np.random.default_rng(5).permutation(64).reshape(8, 8)
+    monkeypatch.setattr(synth, "zipf_draws", lambda *a, **kw: sets.copy())
+    cols = synth.gen_columns(cfg, lay, 8)
+    assert np.array_equal(cols.drawn, sets)
+    L = bqe.upload_layer(lay)
+    y_ref, _, _ = _oracle(lay, cols.x, "bf16")
+    assert_close(_run(bqe, L, cols.x), y_ref, what="65 slots")
+
+
 # ---------------------------------------- decode size, d=4096, f=2048, E=256
 
 @pytest.fixture(scope="module")
