@@ -680,18 +680,30 @@ __host__ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// The product order of a block as two bytes per position (code, bit), for
-// a runtime lookup.
+// The code order of a format packed into four 64-bit words, one byte per
+// product position q (j in bits 0-4, k in bits 5-7), eight positions per
+// word, so that a position known only at run time is found with selects and
+// a shift in registers: indexing a constant array at run time would read it
+// from memory.
 template <int FMT>
-struct CodeOrder {
-  uint8_t j[32], k[32];
-  constexpr CodeOrder() : j(), k() {
-    for (int q = 0; q < 32; ++q) {
-      j[q] = (uint8_t)code_at<FMT>(q).j;
-      k[q] = (uint8_t)code_at<FMT>(q).k;
-    }
+constexpr uint64_t code_order_word(int w) {
+  uint64_t v = 0;
+  for (int b = 0; b < 8; ++b) {
+    const CodeByte c = code_at<FMT>(8 * w + b);
+    v |= (uint64_t)((unsigned)c.j | ((unsigned)c.k << 5)) << (8 * b);
   }
-};
+  return v;
+}
+
+template <int FMT>
+constexpr bool code_order_words_match() {
+  for (int q = 0; q < 32; ++q) {
+    const unsigned byte = (unsigned)(code_order_word<FMT>(q / 8) >> (8 * (q % 8))) & 0xFFu;
+    if ((int)(byte & 31u) != code_at<FMT>(q).j || (int)(byte >> 5) != code_at<FMT>(q).k) return false;
+  }
+  return true;
+}
+static_assert(code_order_words_match<RFPX_FP3>(), "FP3 code order words");
 
 #if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
 // Prepared h of one block of a down matrix of format fmt (a runtime
@@ -714,11 +726,16 @@ __device__ __forceinline__ float prep_h_code_rt(int fmt, const float *hblk, int 
     k1 = code_fp4(p + 16).k;
     o = 7.5f;
   } else {
-    constexpr CodeOrder<RFPX_FP3> ord{};
-    j0 = ord.j[p];
-    k0 = ord.k[p];
-    j1 = ord.j[p + 16];
-    k1 = ord.k[p + 16];
+    // positions p (words 0, 1) and p + 16 (words 2, 3)
+    constexpr uint64_t w0 = code_order_word<RFPX_FP3>(0), w1 = code_order_word<RFPX_FP3>(1);
+    constexpr uint64_t w2 = code_order_word<RFPX_FP3>(2), w3 = code_order_word<RFPX_FP3>(3);
+    const unsigned sh = 8u * (unsigned)(p & 7);
+    const unsigned b0 = (unsigned)((p < 8 ? w0 : w1) >> sh) & 0xFFu;
+    const unsigned b1 = (unsigned)((p < 8 ? w2 : w3) >> sh) & 0xFFu;
+    j0 = (int)(b0 & 31u);
+    k0 = (int)(b0 >> 5);
+    j1 = (int)(b1 & 31u);
+    k1 = (int)(b1 >> 5);
     o = 3.5f;
   }
   const float h0 = hblk[j0], h1 = hblk[j1];
