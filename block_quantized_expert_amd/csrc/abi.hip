@@ -247,8 +247,6 @@ rfpx_status make_plan(const moe_layer *L, int q, int xtype, ForwardPlan *p) {
   off = align_up(off + (size_t)3 * q * nb_d * 4, 256);
   w.hp = off;
   off = align_up(off + (size_t)w.max_slots * q * nb_f * 32 * 4, 256);
-  w.hnc = off;
-  off = align_up(off + (size_t)w.max_slots * q * nb_f * 4, 256);
   w.total = off;
   return RFPX_OK;
 }

@@ -33,11 +33,11 @@
 // descriptor, scalar row offset, 32-bit lane offset), decodes each block in
 // registers once for all columns of the pass (v_dot2 on the prepared
 // pairs), reduces each row across its lanes (DPP and permlane swaps) and
-// writes part sums to LDS.  Then h = silu(g) * u, and the workgroup prepares h for the down
-// matrix (fp32, in the product order of the down format's exact-code decode,
-// CodeGroups in rfpx_impl.hpp) so k_down only loads it; k_down takes each
-// down code as its integer value (v_cvt_f32_ubyte) and adds c * h with fp32
-// FMAs.
+// writes part sums to LDS.  Then h = silu(g) * u, stored as fp32 rows of the
+// slot's h.  k_down loads a lane's blocks of h, puts each block in the
+// product order of its down format's exact-code decode (CodeGroups in
+// rfpx_impl.hpp) in registers, takes each down code as its integer value
+// (v_cvt_f32_ubyte) and adds c * h with fp32 FMAs.
 // Lane geometry (Geo): with a row of >= 64 chunks a wave covers one row per
 // step and lane l reads chunk l (+ 64 for the second part; fully coalesced
 // 1 KiB requests); shorter rows give each wave 64/cpl rows per step.
@@ -52,8 +52,7 @@ struct ExpArgs {
   RouteParams rp;
   const uint32_t *xp;   // prepared activations [fmt][q][nb_d][vx][16]
   const float *xnc;     // [fmt][q][nb_d]
-  uint32_t *hp;         // prepared h [slot][q][nb_f][2][16]
-  float *hnc;           // [slot][q][nb_f]
+  uint32_t *hp;         // h [slot][q][f] (fp32 bits), rows in order
   float *y;
   int d, f, q, nb_d, nb_f;
   int rw_gu, rw_dn;
@@ -202,7 +201,7 @@ __device__ __forceinline__ void unit_compute(const uint32_t (&cw)[R][NM][Fmt<FMT
 }
 
 // The down products of one unit: the unit's rows against GP compact
-// columns of prepared h (fp32, in each block's product order, 32 values per
+// columns of h (fp32, put in each block's product order by prep_h, 32 values per
 // block and column), one exact-code FMA per weight and column (CodeGroups).
 // Rows are decoded one at a time, as in unit_compute.
 template <int FMT, int GP, int R>
@@ -291,14 +290,13 @@ __device__ __forceinline__ void load_prepared_x(const ExpArgs &a, const int (&co
   }
 }
 
-// Prepared h of the blocks of chunk `ch` for G compact columns c0.. of a
-// slot: block b of column c sits at ((c * nb) + b) * 32 words (16 hi, 16
-// lo), its accumulator start at c * nb + b.
+// h of the blocks of chunk `ch` for G compact columns c0.. of a slot, as
+// stored by the gate/up kernel: column c's rows are contiguous fp32 (block
+// b of column c at ((c * nb) + b) * 32 words), element e of a block in word
+// 16 (e / 16) + e % 16 of its register block.
 template <int FMT, int G>
-__device__ __forceinline__ void load_prepared_h(const uint32_t *__restrict__ pw,
-                                                const float *__restrict__ pnc, int nb, int c0,
-                                                int ch, uint32_t (&xr)[G][Fmt<FMT>::CB][2][16],
-                                                float (&ncr)[G][Fmt<FMT>::CB]) {
+__device__ __forceinline__ void load_h(const uint32_t *__restrict__ pw, int nb, int c0, int ch,
+                                       uint32_t (&xr)[G][Fmt<FMT>::CB][2][16]) {
   using F = Fmt<FMT>;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -316,7 +314,40 @@ __device__ __forceinline__ void load_prepared_h(const uint32_t *__restrict__ pw,
           xr[g][j][v][4 * u + 2] = q4.z;
           xr[g][j][v][4 * u + 3] = q4.w;
         }
-      ncr[g][j] = pnc[item];
+    }
+  }
+}
+
+// Blocks of h (as load_h leaves them) into the down products' form, in
+// place: position q of a block holds h[code_at(q).j] * 2^-code_at(q).k (the
+// exact-code products then need no scaling), and the block's accumulator
+// start is -o times the sum of its 32 values (pairwise, in a fixed order).
+template <int FMT, int G>
+__device__ __forceinline__ void prep_h(uint32_t (&xr)[G][Fmt<FMT>::CB][2][16],
+                                       float (&ncr)[G][Fmt<FMT>::CB]) {
+  using F = Fmt<FMT>;
+  constexpr float o = FMT == RFPX_FP2 ? 1.5f : FMT == RFPX_FP3 ? 3.5f : 7.5f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int j = 0; j < F::CB; ++j) {
+      float h[32];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) h[e] = __uint_as_float(xr[g][j][e >> 4][e & 15]);
+      float t[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t[e] = h[2 * e] + h[2 * e + 1];
+#pragma unroll
+      for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+        for (int e = 0; e < w; ++e) t[e] = t[2 * e] + t[2 * e + 1];
+      ncr[g][j] = -o * t[0];
+      static_for<32>([&](auto Q) {
+        constexpr int q = decltype(Q)::value;
+        constexpr CodeByte c = code_at<FMT>(q);
+        constexpr float sc = 1.0f / (float)(1 << c.k);
+        xr[g][j][q >> 4][q & 15] = __float_as_uint(c.k ? h[c.j] * sc : h[c.j]);
+      });
     }
   }
 }
@@ -532,11 +563,12 @@ __device__ __forceinline__ void gateup_pass(const ExpArgs &a, const SlotCols &sc
   }
 }
 
-// h of one gate/up tile of a slot for all of the slot's columns, into
-// hs[c][row] in LDS.
+// h of one gate/up tile of a slot for all of the slot's columns, stored
+// as rows of the slot's h: hout[c * f + row] (the down kernel prepares its
+// blocks in registers).
 template <int FMT, int G, int VX>
 __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc,
-                                            const ExpertDesc &ed, int tile, float *hs,
+                                            const ExpertDesc &ed, int tile, float *hout,
                                             float *gup) {
   constexpr int R = unit_rows_gu(FMT, G);
   const Geo geo = a.geo_gu[FMT];
@@ -585,47 +617,27 @@ __device__ __forceinline__ void gateup_tile(const ExpArgs &a, const SlotCols &sc
         g += gup[((0 * P + pp) * q + c) * rw + row];
         uu += gup[((1 * P + pp) * q + c) * rw + row];
       }
-      hs[c * rw + row] = silu(g) * uu;
+      hout[(size_t)c * a.f + row] = silu(g) * uu;
     }
-    __syncthreads();
+    // the next pass writes gup again
+    if (c0 + GD < sc.ncols) __syncthreads();
   }
 }
 
-// Gate/up tile `tile` of slot `slot`, then h of the tile prepared for the
-// slot's down matrix: 16 threads per (column, block), one pair word each;
-// the block's accumulator start is the sum of the 16 shares (aligned groups
-// of 16 lanes).  LDS: hs [q][rw], then gup [2][2][q][rw].
+// Gate/up tile `tile` of slot `slot`: its rows of h for every column of the
+// slot, into the slot's h in the workspace.  LDS: gup [2][2][q][rw].
 template <int G, int VX>
 __device__ __forceinline__ void gateup_wg(const ExpArgs &a, const SlotCols &sc, int slot,
                                           int tile, float *lds, const ExpertDesc *pre) {
-  float *hs = lds;
-  float *gup = lds + a.q * a.rw_gu;
+  float *gup = lds;
+  float *hout = reinterpret_cast<float *>(a.hp) + (size_t)slot * a.q * a.f + (size_t)tile * a.rw_gu;
   // the expert's planes: from the route table when given, else the image
   const ExpertDesc ed = pre ? *pre : load_desc(a.image, sc.expert);
   const int fmt = ed.fmt[0];
   if (!planned(a.geo_gu, fmt)) return;  // a table that disagrees with fmts
-  if (fmt == RFPX_FP2) gateup_tile<RFPX_FP2, G, VX>(a, sc, ed, tile, hs, gup);
-  else if (fmt == RFPX_FP3) gateup_tile<RFPX_FP3, G, VX>(a, sc, ed, tile, hs, gup);
-  else gateup_tile<RFPX_FP4, G, VX>(a, sc, ed, tile, hs, gup);
-  const int nbt = a.rw_gu / 32;
-  const int fdn = ed.fmt[2];
-  const int nitems = sc.ncols * nbt * 16;
-  for (int base = 0; base < nitems; base += blockDim.x) {
-    const int it = base + threadIdx.x;
-    float share = 0.f;
-    size_t item = 0;
-    if (it < nitems) {
-      const int p = it & 15, cb = it >> 4;
-      const int ci = cb / nbt, bt = cb % nbt;
-      item = ((size_t)slot * a.q + ci) * a.nb_f + tile * nbt + bt;
-      const float *hblk = hs + ci * a.rw_gu + 32 * bt;
-      uint32_t *dst = a.hp + item * 32;
-      share = prep_h_code_rt(fdn, hblk, p, reinterpret_cast<float *>(dst));
-    }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) share += __shfl_xor(share, off, 64);
-    if (it < nitems && (it & 15) == 0) a.hnc[item] = share;
-  }
+  if (fmt == RFPX_FP2) gateup_tile<RFPX_FP2, G, VX>(a, sc, ed, tile, hout, gup);
+  else if (fmt == RFPX_FP3) gateup_tile<RFPX_FP3, G, VX>(a, sc, ed, tile, hout, gup);
+  else gateup_tile<RFPX_FP4, G, VX>(a, sc, ed, tile, hout, gup);
 }
 
 // Gate/up tile blockIdx.x of slot blockIdx.y.  Slot 0 is the shared expert
@@ -758,10 +770,10 @@ __device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, 
   uint32_t cw[R][1][F::CW], sw[R][1];
   unit_load<FMT, 1, R>(mats, cpitch, spitch, r0 + up.rloc_u, geo.rpi, coff, soff, cw, sw);
   const uint32_t *hps = a.hp + (size_t)slot * a.q * a.nb_f * 32;
-  const float *hncs = a.hnc + (size_t)slot * a.q * a.nb_f;
   uint32_t xr[GP][F::CB][2][16];
   float ncr[GP][F::CB];
-  load_prepared_h<FMT, GP>(hps, hncs, a.nb_f, c0, ch, xr, ncr);
+  load_h<FMT, GP>(hps, a.nb_f, c0, ch, xr);
+  prep_h<FMT, GP>(xr, ncr);
   float to[R][1][GP];
   unit_compute_code<FMT, GP, R>(cw, sw, xr, ncr, to);
   const int col0 = sc.col(c0), col1 = GP == 2 ? sc.col(c0 + GP - 1) : col0;
@@ -770,7 +782,7 @@ __device__ __forceinline__ void down_unit(const ExpArgs &a, const SlotCols &sc, 
 }
 
 // The only unit of a slot's down matrix in a one-column step (rows r0 ..
-// r0 + R of the tile, part 0), with the slot's prepared h already in
+// r0 + R of the tile, part 0), with the slot's h already in
 // registers (FP3/FP4: one block per lane): weights, products, and the
 // weighted row results into the wave's accumulator rows.
 template <int FMT>
@@ -798,7 +810,7 @@ __device__ __forceinline__ void down_unit_h(const ExpArgs &a, uint64_t codes, ui
 }
 
 // Units [u0, u1) of one slot's down matrix for GP compact columns c0..,
-// all in column part 0: the wave loads the slot's prepared h of its chunk
+// all in column part 0: the wave loads (and prepares) the slot's h of its chunk
 // once and streams the units with the next unit's code and scale loads in
 // flight while one is decoded (two register sets, used in turn).
 template <int FMT, int GP, int R>
@@ -818,10 +830,10 @@ __device__ __forceinline__ void down_run(const ExpArgs &a, const SlotCols &sc, i
   UnitPos up = unit_pos(u, P, R, geo.rpi);
   unit_load<FMT, 1, R, true>(mats, cpitch, spitch, r0 + up.rloc_u, geo.rpi, coff, soff, cwa, swa);
   const uint32_t *hps = a.hp + (size_t)slot * a.q * a.nb_f * 32;
-  const float *hncs = a.hnc + (size_t)slot * a.q * a.nb_f;
   uint32_t xr[GP][F::CB][2][16];
   float ncr[GP][F::CB];
-  load_prepared_h<FMT, GP>(hps, hncs, a.nb_f, c0, ch, xr, ncr);
+  load_h<FMT, GP>(hps, a.nb_f, c0, ch, xr);
+  prep_h<FMT, GP>(xr, ncr);
   const int col0 = sc.col(c0), col1 = GP == 2 ? sc.col(c0 + GP - 1) : col0;
   const float wgt0 = sc.weight(c0), wgt1 = GP == 2 ? sc.weight(c0 + GP - 1) : wgt0;
   const uint32_t one = one_one_vgpr();
@@ -941,7 +953,7 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
   const int nslots = G == 1 ? a.rp.k + 1 : uniform(a.rt->nslots);
   for (int i = threadIdx.x; i < waves * q * rw; i += blockDim.x) acc[i] = 0.f;
   // One-column steps with one unit per slot and one wave per slot: wave w's
-  // unit is slot w's, and its prepared h (one block per lane, 32 words) does
+  // unit is slot w's, and its h (one block per lane, 32 words) does
   // not depend on the route table.  Waves other than the table reader's
   // load it before the table is read, the table reader right after, so
   // that h is not in flight with the weights.
@@ -953,8 +965,7 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
   // l mod nb_f
   const int hch = (threadIdx.x & 63) % (a.nb_f < 64 ? a.nb_f : 64);
   if (early && wave != 0 && wave < nslots)
-    load_prepared_h<RFPX_FP4, 1>(a.hp + (size_t)wave * a.nb_f * 32, a.hnc + (size_t)wave * a.nb_f,
-                                 a.nb_f, 0, hch, hx, hn);
+    load_h<RFPX_FP4, 1>(a.hp + (size_t)wave * a.nb_f * 32, a.nb_f, 0, hch, hx);
   // the slot table and each slot's down-matrix entry of the image table,
   // all loads in flight together
   for (int i = threadIdx.x; i < nslots * (kQMax + 1); i += blockDim.x) {
@@ -972,7 +983,7 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
       t_w[s][j] = a.rt->w[s][j];
     }
   }
-  if (early && wave == 0) load_prepared_h<RFPX_FP4, 1>(a.hp, a.hnc, a.nb_f, 0, hch, hx, hn);
+  if (early && wave == 0) load_h<RFPX_FP4, 1>(a.hp, a.nb_f, 0, hch, hx);
   __syncthreads();
   const int r0 = blockIdx.x * rw;
   float *accw = acc + wave * q * rw;
@@ -982,10 +993,13 @@ __global__ __launch_bounds__(G == 1 ? 64 * kDnWavesQ1 : 64 * kDnWavesQn) void k_
       const int col0 = uniform(t_cols[wave][0]);
       const float wgt = __int_as_float(uniform(__float_as_int(t_w[wave][0])));
       const uint64_t codes = uniform64(t_codes[wave]), scales = uniform64(t_scales[wave]);
-      if (fmt == RFPX_FP3)
+      if (fmt == RFPX_FP3) {
+        prep_h<RFPX_FP3, 1>(hx, hn);
         down_unit_h<RFPX_FP3>(a, codes, scales, r0, col0, wgt, hx, hn, accw);
-      else if (fmt == RFPX_FP4)
+      } else if (fmt == RFPX_FP4) {
+        prep_h<RFPX_FP4, 1>(hx, hn);
         down_unit_h<RFPX_FP4>(a, codes, scales, r0, col0, wgt, hx, hn, accw);
+      }
     }
   }
   // Steps of several columns: the units of all slots in slot order, cut
@@ -1075,7 +1089,6 @@ ExpArgs make_args(const ForwardPlan &p) {
   a.xp = reinterpret_cast<const uint32_t *>(p.ws + p.wl.xp);
   a.xnc = reinterpret_cast<const float *>(p.ws + p.wl.xnc);
   a.hp = reinterpret_cast<uint32_t *>(p.ws + p.wl.hp);
-  a.hnc = reinterpret_cast<float *>(p.ws + p.wl.hnc);
   a.y = p.y;
   a.d = p.d;
   a.f = p.f;
@@ -1098,7 +1111,7 @@ hipError_t launch_experts(const ForwardPlan &p) {
   const ExpArgs a = make_args(p);
   const dim3 ggu(p.f / p.rw_gu, p.wl.max_slots), gdn(p.d / p.rw_dn);
   const unsigned nt = 64 * p.wmax, ntg = 64 * p.wgu;
-  const size_t lds_gu = ((size_t)ntg + 5 * p.q * p.rw_gu) * sizeof(float);          // sink + hs + gup
+  const size_t lds_gu = ((size_t)ntg + 4 * p.q * p.rw_gu) * sizeof(float);          // sink + gup
   const size_t lds_dn = ((size_t)nt + (size_t)p.wmax * p.q * p.rw_dn) * sizeof(float);  // sink + acc
   const bool bf = p.xtype == RFPX_X_BF16;
   hipEvent_t *ev = (hipEvent_t *)p.events;

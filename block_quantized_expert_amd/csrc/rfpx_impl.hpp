@@ -150,8 +150,7 @@ struct WsLayout {
   size_t scores;    // fp32 [q][E]
   size_t xp;        // u32  [3 fmts][q][nb_d][vx][16]  prepared activations
   size_t xnc;       // fp32 [3][q][nb_d]               their accumulator starts
-  size_t hp;        // fp32 [slots][q][nb_f][32]       prepared h (exact-code order)
-  size_t hnc;       // fp32 [slots][q][nb_f]
+  size_t hp;        // fp32 [slots][q][f]              h rows
   size_t total;
   int max_slots;
 };
@@ -639,24 +638,6 @@ constexpr CodeByte code_at(int q) {
   return CodeByte{-1, 0};
 }
 
-// The same order in closed form for FP2 (group g = 4t + u holds codes 16t +
-// 4i + u at bit 2u) and FP4 (group g = 2t + odd holds codes 8t + 2i + odd at
-// bit 4 odd); position q = 4g + i.
-__host__ __device__ constexpr CodeByte code_fp2(int q) {
-  return CodeByte{(int8_t)(16 * (q >> 4) + 4 * (q & 3) + ((q >> 2) & 3)), (int8_t)(2 * ((q >> 2) & 3))};
-}
-__host__ __device__ constexpr CodeByte code_fp4(int q) {
-  return CodeByte{(int8_t)(8 * (q >> 3) + 2 * (q & 3) + ((q >> 2) & 1)), (int8_t)(4 * ((q >> 2) & 1))};
-}
-constexpr bool closed_forms_match() {
-  for (int q = 0; q < 32; ++q) {
-    if (code_fp2(q).j != code_at<RFPX_FP2>(q).j || code_fp2(q).k != code_at<RFPX_FP2>(q).k) return false;
-    if (code_fp4(q).j != code_at<RFPX_FP4>(q).j || code_fp4(q).k != code_at<RFPX_FP4>(q).k) return false;
-  }
-  return true;
-}
-static_assert(closed_forms_match(), "closed-form product order");
-
 // Product position of byte b of group gi (the number of codes before it).
 template <int FMT>
 constexpr int code_pos(int gi, int b) {
@@ -679,71 +660,6 @@ template <int N, typename F>
 __host__ __device__ __forceinline__ void static_for(F &&f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
-
-// The code order of a format packed into four 64-bit words, one byte per
-// product position q (j in bits 0-4, k in bits 5-7), eight positions per
-// word, so that a position known only at run time is found with selects and
-// a shift in registers: indexing a constant array at run time would read it
-// from memory.
-template <int FMT>
-constexpr uint64_t code_order_word(int w) {
-  uint64_t v = 0;
-  for (int b = 0; b < 8; ++b) {
-    const CodeByte c = code_at<FMT>(8 * w + b);
-    v |= (uint64_t)((unsigned)c.j | ((unsigned)c.k << 5)) << (8 * b);
-  }
-  return v;
-}
-
-template <int FMT>
-constexpr bool code_order_words_match() {
-  for (int q = 0; q < 32; ++q) {
-    const unsigned byte = (unsigned)(code_order_word<FMT>(q / 8) >> (8 * (q % 8))) & 0xFFu;
-    if ((int)(byte & 31u) != code_at<FMT>(q).j || (int)(byte >> 5) != code_at<FMT>(q).k) return false;
-  }
-  return true;
-}
-static_assert(code_order_words_match<RFPX_FP3>(), "FP3 code order words");
-
-#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
-// Prepared h of one block of a down matrix of format fmt (a runtime
-// value), two product positions per lane (p and p + 16 of the block's 16
-// lanes): dst[q] = h[code_at(q).j] * 2^-code_at(q).k.  Returns the lane's
-// share of the block's accumulator start, -o times its two h values.
-__device__ __forceinline__ float prep_h_code_rt(int fmt, const float *hblk, int p, float *dst) {
-  int j0, k0, j1, k1;
-  float o;
-  if (fmt == RFPX_FP2) {
-    j0 = code_fp2(p).j;
-    k0 = code_fp2(p).k;
-    j1 = code_fp2(p + 16).j;
-    k1 = code_fp2(p + 16).k;
-    o = 1.5f;
-  } else if (fmt == RFPX_FP4) {
-    j0 = code_fp4(p).j;
-    k0 = code_fp4(p).k;
-    j1 = code_fp4(p + 16).j;
-    k1 = code_fp4(p + 16).k;
-    o = 7.5f;
-  } else {
-    // positions p (words 0, 1) and p + 16 (words 2, 3)
-    constexpr uint64_t w0 = code_order_word<RFPX_FP3>(0), w1 = code_order_word<RFPX_FP3>(1);
-    constexpr uint64_t w2 = code_order_word<RFPX_FP3>(2), w3 = code_order_word<RFPX_FP3>(3);
-    const unsigned sh = 8u * (unsigned)(p & 7);
-    const unsigned b0 = (unsigned)((p < 8 ? w0 : w1) >> sh) & 0xFFu;
-    const unsigned b1 = (unsigned)((p < 8 ? w2 : w3) >> sh) & 0xFFu;
-    j0 = (int)(b0 & 31u);
-    k0 = (int)(b0 >> 5);
-    j1 = (int)(b1 & 31u);
-    k1 = (int)(b1 >> 5);
-    o = 3.5f;
-  }
-  const float h0 = hblk[j0], h1 = hblk[j1];
-  dst[p] = h0 * __uint_as_float((uint32_t)(127 - k0) << 23);
-  dst[p + 16] = h1 * __uint_as_float((uint32_t)(127 - k1) << 23);
-  return -o * (h0 + h1);
-}
-#endif
 
 // Block scale as an fp32 multiplier: fp16 bits (FP2/FP3) or E8M0 (FP4).
 template <int FMT>
