@@ -177,7 +177,7 @@ def host_description() -> dict:
 
 def oracle_threads() -> int:
     """Threads for the multi-core oracle leg: every core this process may
-    use, at most 16 (a GPU machine's CPU share)."""
+    use, at most 16 (the host share of one GPU on a shared node)."""
     return max(1, min(16, host_description()["nproc"]))
 
 

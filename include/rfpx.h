@@ -95,7 +95,7 @@ typedef enum {
   RFPX_E_HIP = -6        /* a HIP call failed */
 } rfpx_status;
 
-/* Limits of this build. */
+/* Compile-time limits of the library. */
 #define RFPX_Q_MAX 8    /* verify columns per decode call */
 #define RFPX_K_MAX 8    /* routed experts per column */
 #define RFPX_E_MAX 1024 /* routed experts per layer */
