@@ -731,16 +731,14 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
         }
       }
     };
-    if (c * KC + KC <= nblocks) {
-      // a full chunk: no per-block bounds branch (unrolling further raises
-      // the registers past two waves per SIMD and measures slower)
+    // one loop with the chunk's block count as its trip count: a separate
+    // loop for a partial last chunk made the compiler copy every
+    // accumulator register into and out of the full-chunk loop at each
+    // chunk (unrolling further raises the registers past two waves per SIMD
+    // and measures slower)
+    const int jn = min(KC, nblocks - c * KC);
 #pragma unroll 1
-      for (int j = 0; j < KC; ++j) block(j);
-    } else {
-#pragma unroll 1
-      for (int j = 0; j < KC; ++j)
-        if (c * KC + j < nblocks) block(j);
-    }
+    for (int j = 0; j < jn; ++j) block(j);
     if (c + 1 < nchunks) {
       store_a((c + 1) & 1);
       if ((c + 1) % CPS == 0) {
