@@ -120,16 +120,21 @@ def expert_bytes(lay, e):
     return tot, gu
 
 
-KERNEL_SOURCES = ("expert.hip", "prefill.hip", "route.hip", "dense.hip", "rfpx_impl.hpp",
-                  "rfpx_route.hpp", "abi.hip")
+# The sources that define each product kernel's code and launch (the files
+# its code and its launch set-up are built from): a counter summary stays
+# valid while these are unchanged.
+_DECODE_SOURCES = ("expert.hip", "route.hip", "rfpx_impl.hpp", "rfpx_route.hpp", "abi.hip")
+_PREFILL_SOURCES = ("prefill.hip", "rfpx_impl.hpp", "rfpx_route.hpp", "abi.hip")
+KERNEL_SOURCES = {"k_gateup": _DECODE_SOURCES, "k_down": _DECODE_SOURCES,
+                  "k_pf_gateup": _PREFILL_SOURCES, "k_pf_down": _PREFILL_SOURCES}
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the sources that define the layer kernels and their launch."""
+def kernel_source_hash(kernel: str, root: str = ROOT) -> str:
+    """sha256 over the sources that define `kernel` and its launch."""
     import hashlib
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        path = os.path.join(ROOT, "block_quantized_expert_amd", "csrc", name)
+    for name in KERNEL_SOURCES[kernel]:
+        path = os.path.join(root, "block_quantized_expert_amd", "csrc", name)
         if os.path.exists(path):
             with open(path, "rb") as fh:
                 h.update(fh.read())
@@ -149,7 +154,7 @@ def measured_traffic(kernel: str, workload: str):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != kernel_source_hash():
+    if kernel not in KERNEL_SOURCES or kv.get("source_sha256") != kernel_source_hash(kernel):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
