@@ -604,8 +604,11 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
     }
   const int nchunks = (nblocks + KC - 1) / KC;
   const int nspans = (nblocks + BS::SB - 1) / BS::SB;
-  u32x4 ra[NLD];
-  float rnc = 0.f;
+  // A words (and accumulator starts) in flight two chunks ahead, in two
+  // register sets: a chunk's loads go out two chunks before their LDS store,
+  // so that they have two chunks of products to arrive in
+  u32x4 ra0[NLD], ra1[NLD];
+  float rnc0 = 0.f, rnc1 = 0.f;
   u32x4 rb[BS::NB];
 
   auto issue_b = [&](int sp) __attribute__((always_inline)) {
@@ -643,7 +646,14 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
         *reinterpret_cast<u32x4 *>(lds_b + rr * BS::PITCH + 16 + 16 * p) = rb[q];
     }
   };
-  auto issue_a = [&](int c) __attribute__((always_inline)) {
+  // chunk c's A loads (and accumulator starts), every load unconditional: a
+  // chunk past the last re-reads the last block, and a thread without an
+  // accumulator start re-reads one.  Every store of a loaded value is
+  // unconditional too (a thread without an accumulator start stores it to
+  // its LDS sink word): a load or a use behind a branch leaves the load
+  // pending on the other path, and the compiler then waits for every load
+  // in flight before the next write to its registers.
+  auto issue_a = [&](int c, u32x4 (&ra)[NLD], float &rnc) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int item = tid + kPfThreads * q;
@@ -653,14 +663,15 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
       ra[q] = __builtin_amdgcn_raw_buffer_load_b128(
           ar, (int)(rows.a_row[r] + blk * a_stride + 16 * w4), 0, 0);
     }
-    if (tid < KC * ROWS) {
-      const int r = tid % ROWS, j = tid / ROWS;
+    {
+      const int t = min(tid, KC * ROWS - 1);
+      const int r = t % ROWS, j = t / ROWS;
       const int blk = min(c * KC + j, nblocks - 1);
       rnc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                           ncr, (int)(rows.nc_row[r] + blk * nc_stride), 0, 0));
     }
   };
-  auto store_a = [&](int buf) __attribute__((always_inline)) {
+  auto store_a = [&](int buf, const u32x4 (&ra)[NLD], float rnc) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < NLD; ++q) {
       const int item = tid + kPfThreads * q;
@@ -668,18 +679,25 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
       const int j = pc / V4, w4 = pc % V4;
       *reinterpret_cast<u32x4 *>(lds_a + ((buf * KC + j) * ROWS + r) * AWP + 4 * w4) = ra[q];
     }
-    if (tid < KC * ROWS) lds_nc[buf * KC * ROWS + tid] = rnc;
+    // (a thread past the starts writes past both buffers' starts, inside
+    // the 2 x 4 x kChunk words of the region: KC x ROWS <= kPfThreads)
+    lds_nc[tid < KC * ROWS ? buf * KC * ROWS + tid : KC * ROWS + tid] = rnc;
   };
 
   issue_b(0);
-  issue_a(0);
+  issue_a(0, ra0, rnc0);
+  issue_a(1, ra1, rnc1);
   store_b();
   if (nspans > 1) issue_b(1);
-  store_a(0);
+  store_a(0, ra0, rnc0);
   __syncthreads();
   const uint32_t one = one_one_vgpr();
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) issue_a(c + 1);
+  // chunk c: its A words are in LDS buffer c & 1; chunk c + 1's are in
+  // flight in `rnext`; chunk c + 2's loads go out into `rfree` (the set
+  // chunk c came from)
+  auto chunk = [&](int c, u32x4 (&rfree)[NLD], float &ncfree, const u32x4 (&rnext)[NLD],
+                   const float &ncnext) __attribute__((always_inline)) {
+    issue_a(c + 2, rfree, ncfree);
     const int buf = c & 1;
     const int jb0 = (c % CPS) * KC;
     // shift of this span's scales within their first piece
@@ -739,8 +757,10 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
     const int jn = min(KC, nblocks - c * KC);
 #pragma unroll 1
     for (int j = 0; j < jn; ++j) block(j);
+    // (stored also after the last chunk, where nobody reads that buffer: an
+    // unconditional use keeps the compiler's waits for the next set exact)
+    store_a((c + 1) & 1, rnext, ncnext);
     if (c + 1 < nchunks) {
-      store_a((c + 1) & 1);
       if ((c + 1) % CPS == 0) {
         // this wave has finished with its span: refill it, ask for the next
         const int sp = (c + 1) / CPS;
@@ -749,6 +769,14 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
       }
     }
     __syncthreads();
+  };
+  // chunks in pairs with no test between them: for an odd chunk count the
+  // last pair's second chunk has no blocks (its loads re-read the last
+  // block and nobody reads what it stores), so that every load of a set is
+  // used on every path and the compiler's waits stay exact
+  for (int c = 0; c < nchunks; c += 2) {
+    chunk(c, ra0, rnc0, ra1, rnc1);
+    chunk(c + 1, ra1, rnc1, ra0, rnc0);
   }
 }
 
