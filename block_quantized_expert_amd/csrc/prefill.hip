@@ -770,7 +770,8 @@ __device__ __forceinline__ void pf_gemm(const PfArgs &a, int nblocks,
     }
     __syncthreads();
   };
-  // chunks in pairs with no test between them: for an odd chunk count the
+  // chunks in pairs with no test between them: for an odd chunk count (one
+  // chunk: d and f are powers of two, so a count above one is even) the
   // last pair's second chunk has no blocks (its loads re-read the last
   // block and nobody reads what it stores), so that every load of a set is
   // used on every path and the compiler's waits stay exact
